@@ -1,0 +1,58 @@
+"""CPU test: the pins are strong enough to catch plausible oracle mistakes.
+
+Each mutant is a copy of oracle/mla_oracle.c with one deliberate error (a
+dropped term, a wrong sign or index, a transposed operand, a wrong slice),
+compiled with gcc into a temporary directory.  The real oracle passes every
+pin; each mutant must fail at least one.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mla_oracle.c")
+
+MUTANTS = {
+    "drop_rotary_term": ("s[j] = (lat + rot) * scale;", "s[j] = (lat) * scale;"),
+    "drop_scale": ("s[j] = (lat + rot) * scale;", "s[j] = (lat + rot);"),
+    "transpose_w_uk": ("qn[d] * w_uk[d * Dc + c]", "qn[d] * w_uk[c * Dn + d]"),
+    "transpose_w_uv": ("mix[c] * w_uv[d * Dc + c]", "mix[c] * w_uv[c * Dv + d]"),
+    "w_uv_from_w_uk_rows": ("(h * rows_per_head + Dn) * Dc", "(h * rows_per_head) * Dc"),
+    "softmax_sign": ("denom += exp(s[j] - m)", "denom += exp(m - s[j])"),
+    "mix_wrong_row": ("const double* crow = kv + b * kv_sb + set[j] * kv_st;\n                for (int64_t c = 0; c < Dc; ++c) mix",
+                      "const double* crow = kv + b * kv_sb + set[0] * kv_st;\n                for (int64_t c = 0; c < Dc; ++c) mix"),
+    "mask_off_by_one": ("mark[t] = 1;", "mark[t > 0 ? t - 1 : t] = 1;"),
+    "rotary_uses_latent": ("const double* prow = pe + b * pe_sb + set[j] * pe_st;",
+                           "const double* prow = kv + b * kv_sb + set[j] * kv_st;"),
+    "lse_without_log": ("m + log(denom)", "m + denom"),
+    "head_stride_q_pe": ("q_pe + (b * H + h) * Dr", "q_pe + (b * H) * Dr"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    so = tmp_path / f"{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(src), "-lm"])
+    return oracle.load(str(so))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_fails_a_pin(tmp_path, name):
+    lib = _build_mutant(tmp_path, name, *MUTANTS[name])
+
+    def dec(**kw):
+        return oracle.decode(**kw, lib=lib)
+
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(dec)
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
