@@ -1,0 +1,199 @@
+/*
+ * libmla_decode: absorbed-weight sparse multi-head latent attention decode
+ * step for MI355X (gfx950), as a C ABI.
+ *
+ * The step (DeepSeek-V3.2-Exp pages, decode mode):
+ *   1. mla_absorb_q       q~[b,h,:] = q_nope[b,h,:] W_UK,h          (128 -> 512)
+ *      "Query-key similarity" page, decode-branch code excerpt: the query is
+ *      absorbed through the first 128 rows of each head's wkv_b slice.
+ *   2. mla_sparse_decode  s[b,h,t] = scale * (q~ . c[b,t] + q_pe . k_pe[b,t])
+ *      over the selected positions only, softmax over keys, and the latent
+ *      mix O~[b,h,:] = sum_t A[b,h,t] c[b,t,:]
+ *      "Query-key similarity" page, formula S_i and the index mask in the code
+ *      excerpt (-inf off the indexer's selection, shared by all heads);
+ *      "Softmax" page, formula for A (normalisation over key positions).
+ *   3. mla_combine        merges split-K partials of step 2 (log-sum-exp).
+ *   4. mla_value_up       O[b,h,:] = O~[b,h,:] W_UV,h^T               (512 -> 128)
+ *      "Apply value weights" page, formula O_i = O~_i W_UV,i.
+ *
+ * Fixed dimensions (Queries page, init excerpt and shapes): 128 heads,
+ * 128 non-rotary and 64 rotary query dims (qk_head_dim 192), latent rank 512,
+ * value dim 128.  wkv_b is the [128*256, 512] matrix of the key-value
+ * up-projection; per head h, rows h*256 .. h*256+127 are W_UK,h and rows
+ * h*256+128 .. h*256+255 are W_UV,h, each stored [d][c] with c contiguous.
+ *
+ * Conventions
+ *  - bf16 tensors are passed as raw 16-bit storage (void*).  All strides are
+ *    in elements.  Every tensor pointer is GPU device memory owned by the
+ *    caller; the library allocates and frees nothing and keeps no pointer
+ *    after a call returns.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and never synchronise.  Inputs must not alias outputs.
+ *  - Every entry point returns MLA_OK (0) or a positive mla_status.  Argument
+ *    errors are detected on the host before anything is enqueued.  No C++
+ *    exception crosses this interface and the library never aborts.
+ *  - The library is reentrant; its only global state is a per-device cache of
+ *    the compute-unit count.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+#define MLA_HEADS 128
+#define MLA_NOPE_DIM 128
+#define MLA_ROPE_DIM 64
+#define MLA_LATENT_DIM 512
+#define MLA_VALUE_DIM 128
+
+/* Most index slots one split may hold in sparse mode (indices != NULL). */
+#define MLA_MAX_SLOTS_PER_SPLIT 2048
+#define MLA_MAX_SPLITS 64
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                     */
+  MLA_ERR_BAD_DIM = 2,             /* B, k_max, max_len, splits or head groups invalid */
+  MLA_ERR_ALIGNMENT = 3,           /* base not 16-byte aligned / stride not 8 elements */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < mla_workspace_bytes(B, num_splits)   */
+  MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths     */
+  MLA_ERR_HIP = 6,                 /* a HIP call failed: see mla_last_hip_error()     */
+  MLA_ERR_RANGE = 7                /* one sequence's cache span exceeds 2 GiB         */
+} mla_status;
+
+/* Flags of mla_sparse_decode. */
+#define MLA_FLAG_VALIDATE 1u      /* range/duplicate/empty checks + attended bitmap */
+#define MLA_FLAG_WRITE_SCORES 2u  /* write the scaled scores of every index slot   */
+
+/* Bits OR-ed into *status_dev by the device-side checks (MLA_FLAG_VALIDATE). */
+#define MLA_DEV_INDEX_OUT_OF_RANGE 1u /* an index >= L_b, or negative and not -1 */
+#define MLA_DEV_DUPLICATE_INDEX 2u    /* a position appears twice in one row     */
+#define MLA_DEV_EMPTY_SELECTION 4u    /* a sequence selects no position          */
+
+int mla_abi_version(void);
+const char* mla_status_string(int status);
+/* The hipError_t of the most recent MLA_ERR_HIP on this thread (0 if none). */
+int mla_last_hip_error(void);
+
+/*
+ * Launch plan for mla_sparse_decode: how many key splits per sequence and how
+ * many head groups (1: a workgroup handles all 128 heads; 2: 64 heads each,
+ * the two groups of one sequence share its gathered rows through L2).
+ * `dense` is nonzero when no index list is passed.  num_cus <= 0 means 256.
+ * Pure host function.  Returns MLA_ERR_BAD_DIM for B < 1 or k_max < 1.
+ */
+int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus,
+             int32_t* num_splits, int32_t* head_groups);
+
+/*
+ * Bytes of workspace mla_sparse_decode needs for `num_splits` splits: 0 when
+ * num_splits == 1 (the normalised result is written directly), otherwise the
+ * fp32 partial mixes [S][B][128][512] and the per-head (max, sum) pairs
+ * [S][B][128][2].  Returns 0 for invalid arguments.
+ */
+size_t mla_workspace_bytes(int32_t B, int32_t num_splits);
+
+/*
+ * Step 1: q_abs[b][h][c] = sum_d q_nope[b][h][d] * W_UK,h[d][c].
+ *   q_nope  bf16, element (b, h, d) at q_nope[b*q_nope_sb + h*q_nope_sh + d]
+ *           (d contiguous; the [B,1,128,128] layout has sb = 16384, sh = 128).
+ *   wkv_b   bf16 [32768][512], contiguous.
+ *   q_abs   bf16 [B][128][512], contiguous (written).
+ * Requires 1 <= B <= 65536, 16-byte aligned bases, strides multiples of 8.
+ * fp32 accumulation, one rounding to bf16.
+ */
+int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
+                 const void* wkv_b, void* q_abs, int32_t B, void* stream);
+
+/*
+ * Step 2: sparse flash-decode over the selected cache rows.
+ *   q_abs    bf16 [B][128][512] contiguous (from mla_absorb_q).
+ *   q_pe     bf16, element (b, h, r) at q_pe[b*q_pe_sb + h*q_pe_sh + r], r < 64.
+ *   kv       latent cache: row (b, t) at kv + b*kv_sb + t*kv_st, 512 values.
+ *   pe       rotary-key cache: row (b, t) at pe + b*pe_sb + t*pe_st, 64 values.
+ *            Two buffers as in the pages' code, or one packed 576-value row
+ *            (pe = kv + 512, pe_st = kv_st) -- both are plain strides here.
+ *   seq_lens int32 [B], device: L_b, the cached positions of sequence b
+ *            (clamped to [0, max_len]).
+ *   max_len  host upper bound on every L_b.
+ *   indices  int32 [B][k_max], device, any order: the selected positions of
+ *            each sequence, shared by all heads; -1 is padding and is skipped.
+ *            Positions must be distinct and < L_b (a top-k's output).  NULL
+ *            selects every t < L_b (dense decode; then k_max >= max_len).
+ *   k_max    index slots per sequence.
+ *   scale    softmax scale (qk_head_dim^-1/2 for this model).
+ *   num_splits, head_groups   from mla_plan (1 <= S <= 64, groups 1 or 2).
+ *            In sparse mode each split holds at most MLA_MAX_SLOTS_PER_SPLIT
+ *            slots (ceil(k_max / S) rounded up to 32 * head_groups).
+ *   workspace, ws_bytes       device scratch, >= mla_workspace_bytes(B, S);
+ *            unused (may be NULL) when S == 1.
+ *   o_latent bf16 [B][128][512], lse fp32 [B][128] (natural log; may be NULL):
+ *            written here when S == 1, by mla_combine when S > 1.
+ *   flags    MLA_FLAG_*.
+ *   attended_bitmap uint32 [B][bitmap_words], zeroed by the caller: with
+ *            VALIDATE, bit t of row b is set for every selected in-range
+ *            position (written by the gather itself).  bitmap_words >=
+ *            ceil(max_len / 32).
+ *   scores_out fp32 [B][128][k_max]: with WRITE_SCORES, scale * (q~ . c +
+ *            q_pe . k_pe) of each slot's position, -inf for masked slots.
+ *   status_dev uint32, device, zeroed by the caller: MLA_DEV_* bits (VALIDATE).
+ * Without VALIDATE, rows with repeated indices are attended once per repeat
+ * and out-of-range indices are skipped; both are caller errors.
+ * Each sequence's cache span (max_len * row stride * 2 bytes, for kv and pe)
+ * must be below 2 GiB (MLA_ERR_RANGE).
+ */
+int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                      const void* kv, int64_t kv_sb, int64_t kv_st,
+                      const void* pe, int64_t pe_sb, int64_t pe_st,
+                      const int32_t* seq_lens, int32_t max_len,
+                      const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                      int32_t num_splits, int32_t head_groups,
+                      void* workspace, size_t ws_bytes,
+                      void* o_latent, float* lse,
+                      uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                      float* scores_out, uint32_t* status_dev, void* stream);
+
+/*
+ * Step 3: merge the S partials of step 2 ("Softmax" page: the normalisation
+ * over all selected keys, assembled from per-split maxima and sums):
+ *   O~ = sum_s w_s acc_s / sum_s w_s l_s,  w_s = 2^(m_s - max_s m_s),
+ *   lse = ln 2 * (max_s m_s + log2 sum_s w_s l_s).
+ * A no-op returning MLA_OK when num_splits == 1.  An empty selection gives
+ * NaN in o_latent and -inf in lse; with status_dev non-NULL it also sets
+ * MLA_DEV_EMPTY_SELECTION.
+ */
+int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                void* o_latent, float* lse, uint32_t* status_dev, void* stream);
+
+/*
+ * Step 4: out[b][h][d] = sum_c o_latent[b][h][c] * W_UV,h[d][c].
+ *   o_latent bf16 [B][128][512] contiguous; wkv_b as in mla_absorb_q;
+ *   out bf16, element (b, h, d) at out[b*out_sb + h*out_sh + d] (the
+ *   [B,1,128,128] layout has sb = 16384, sh = 128).
+ * fp32 accumulation, one rounding to bf16.
+ */
+int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
+                 int64_t out_sb, int64_t out_sh, int32_t B, void* stream);
+
+/*
+ * One-time set-up ("Query-key similarity" page, code excerpt: a quantised
+ * wkv_b is dequantised once and the dense copy reused):
+ *   w_bf16[i][j] = bf16(e4m3(w_fp8[i][j]) * scales[i/128][j/128]), rounded to
+ * nearest even from the exact product.
+ *   w_fp8   uint8 [32768][512] OCP E4M3FN codes; scales fp32 [256][4];
+ *   w_bf16  bf16 [32768][512] (written).
+ */
+int mla_dequant_wkv_b_fp8(const void* w_fp8, const float* scales, void* w_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -20,6 +20,8 @@ from .core import (  # noqa: F401
     build,
     load,
     decode,
+    absorb,
+    value_up,
     dequant_fp8,
     e4m3_to_double,
     bf16_bits_to_double,

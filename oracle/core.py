@@ -62,6 +62,10 @@ def load(path: str | None = None):
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_double_to_bf16.argtypes = [d]
+        lib.oracle_absorb.restype = ctypes.c_int
+        lib.oracle_absorb.argtypes = [i64, i64, i64, i64, i64, p, p, p]
+        lib.oracle_value_up.restype = ctypes.c_int
+        lib.oracle_value_up.argtypes = [i64, i64, i64, i64, i64, p, p, p]
         if path is not None:
             return lib
         _lib = lib
@@ -159,6 +163,40 @@ def decode(q_nope, q_pe, kv, pe, wkv_b, seq_lens, indices, scale,
     if att is not None:
         res["attended"] = att
     return res
+
+
+def _bhd(x):
+    a = _f64(x)
+    if a.ndim == 4:
+        a = a.reshape(a.shape[0], a.shape[2], a.shape[3])
+    return np.ascontiguousarray(a)
+
+
+def absorb(q_nope, wkv_b, lib=None):
+    """Step 2 alone: q_abs [B,H,Dc] from q_nope [B,H,Dn] (or [B,1,H,Dn])."""
+    lib = lib or load()
+    q = _bhd(q_nope)
+    w = _f64(wkv_b)
+    B, H, Dn = q.shape
+    Dc = w.shape[1]
+    Dv = w.shape[0] // H - Dn
+    out = np.empty((B, H, Dc))
+    if lib.oracle_absorb(B, H, Dn, Dc, Dv, _ptr(q), _ptr(w), _ptr(out)):
+        raise ValueError("oracle_absorb: bad arguments")
+    return out
+
+
+def value_up(o_lat, wkv_b, Dn=128, lib=None):
+    """Step 7 alone: out [B,H,Dv] from o_lat [B,H,Dc]."""
+    lib = lib or load()
+    o = _bhd(o_lat)
+    w = _f64(wkv_b)
+    B, H, Dc = o.shape
+    Dv = w.shape[0] // H - Dn
+    out = np.empty((B, H, Dv))
+    if lib.oracle_value_up(B, H, Dn, Dc, Dv, _ptr(o), _ptr(w), _ptr(out)):
+        raise ValueError("oracle_value_up: bad arguments")
+    return out
 
 
 def dequant_fp8(w_fp8, scales, block=128):

@@ -259,3 +259,47 @@ int oracle_decode(int64_t B, int64_t H, int64_t Dn, int64_t Dc, int64_t Dr,
     }
     return status;
 }
+
+/*
+ * Step 2 alone ("Query-key similarity" page, code excerpt, absorption):
+ *   q_abs[b][h][c] = sum_d q_nope[b][h][d] * W_UK,h[d][c]
+ * q_nope [B][H][Dn]; wkv_b as in oracle_decode; q_abs [B][H][Dc].
+ */
+int oracle_absorb(int64_t B, int64_t H, int64_t Dn, int64_t Dc, int64_t Dv,
+                  const double* q_nope, const double* wkv_b, double* q_abs) {
+    if (B <= 0 || H <= 0 || Dn <= 0 || Dc <= 0 || Dv <= 0 || !q_nope || !wkv_b || !q_abs)
+        return ORACLE_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t h = bh % H;
+        const double* w_uk = wkv_b + (h * (Dn + Dv)) * Dc;
+        for (int64_t c = 0; c < Dc; ++c) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < Dn; ++d) acc += q_nope[bh * Dn + d] * w_uk[d * Dc + c];
+            q_abs[bh * Dc + c] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Step 7 alone ("Apply value weights" page, formula O_i = O~_i W_UV,i, with
+ * W_UV,i the transpose of the stored [d][c] slice):
+ *   out[b][h][d] = sum_c o_lat[b][h][c] * W_UV,h[d][c]
+ */
+int oracle_value_up(int64_t B, int64_t H, int64_t Dn, int64_t Dc, int64_t Dv,
+                    const double* o_lat, const double* wkv_b, double* out) {
+    if (B <= 0 || H <= 0 || Dn <= 0 || Dc <= 0 || Dv <= 0 || !o_lat || !wkv_b || !out)
+        return ORACLE_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t h = bh % H;
+        const double* w_uv = wkv_b + (h * (Dn + Dv) + Dn) * Dc;
+        for (int64_t d = 0; d < Dv; ++d) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < Dc; ++c) acc += o_lat[bh * Dc + c] * w_uv[d * Dc + c];
+            out[bh * Dv + d] = acc;
+        }
+    }
+    return ORACLE_OK;
+}

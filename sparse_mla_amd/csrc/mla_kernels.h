@@ -1,0 +1,85 @@
+// Internal interface between the C-ABI entry points (mla_api.cpp) and the
+// HIP kernels (mla_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kHeads = 128;
+constexpr int kNope = 128;
+constexpr int kRope = 64;
+constexpr int kLatent = 512;
+constexpr int kValue = 128;
+constexpr int kRowsPerHead = kNope + kValue;  // 256 rows of wkv_b per head
+constexpr int kIdxCap = 2048;                  // index slots staged per split
+
+struct AbsorbArgs {
+  const uint16_t* q_nope;
+  int64_t q_sb, q_sh;
+  const uint16_t* wkv_b;
+  uint16_t* q_abs;
+  int32_t B;
+};
+
+struct DecodeArgs {
+  const uint16_t* q_abs;
+  const uint16_t* q_pe;
+  int64_t q_pe_sb, q_pe_sh;
+  const uint16_t* kv;
+  int64_t kv_sb, kv_st;
+  const uint16_t* pe;
+  int64_t pe_sb, pe_st;
+  const int32_t* seq_lens;
+  const int32_t* indices;   // NULL: dense
+  int32_t max_len;
+  int32_t k_max;
+  int32_t chunk;            // index slots per split (multiple of 32 * head groups)
+  int32_t B;
+  int32_t S;                // splits
+  float scale;              // softmax scale
+  float scale_log2;         // softmax scale * log2(e)
+  float* part_acc;          // [S][B][128][512] when S > 1
+  float* part_ml;           // [S][B][128][2]   when S > 1
+  uint16_t* o_latent;       // [B][128][512]    when S == 1
+  float* lse;               // [B][128]         when S == 1 (may be NULL)
+  uint32_t flags;
+  uint32_t* bitmap;
+  int64_t bitmap_words;
+  float* scores;            // [B][128][k_max]
+  uint32_t* status;
+};
+
+struct CombineArgs {
+  const float* part_acc;
+  const float* part_ml;
+  int32_t B, S;
+  uint16_t* o_latent;
+  float* lse;
+  uint32_t* status;
+};
+
+struct ValueUpArgs {
+  const uint16_t* o_latent;
+  const uint16_t* wkv_b;
+  uint16_t* out;
+  int64_t out_sb, out_sh;
+  int32_t B;
+};
+
+struct DequantArgs {
+  const uint8_t* w;
+  const float* scales;
+  uint16_t* out;
+};
+
+// Each returns a hipError_t value (0 on success).
+int launch_absorb(const AbsorbArgs& a, void* stream);
+int launch_decode(const DecodeArgs& a, int head_groups, void* stream);
+int launch_combine(const CombineArgs& a, void* stream);
+int launch_value_up(const ValueUpArgs& a, void* stream);
+int launch_dequant(const DequantArgs& a, void* stream);
+int device_cu_count(int* cus);
+
+}  // namespace mla

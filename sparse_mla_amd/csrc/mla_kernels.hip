@@ -1,0 +1,637 @@
+// HIP kernels of the absorbed sparse MLA decode step, written for CDNA4
+// (gfx950): 64-wide wavefronts, bf16 MFMA 32x32x16, LDS transpose reads and
+// buffer loads that write straight into LDS.
+//
+// Operation (DeepSeek-V3.2-Exp pages, decode mode):
+//   absorb   q~ = q_nope W_UK,h          "Query-key similarity" page, code excerpt
+//   decode   s = scale (q~ c^T + q_pe k_pe^T) on the selected rows, softmax over
+//            keys, O~ = A c                "Query-key similarity" page, formula
+//            S_i and index mask; "Softmax" page, formula for A
+//   combine  log-sum-exp merge of key-split partials
+//   value-up O = O~ W_UV,h^T               "Apply value weights" page, formula O_i
+//
+// MFMA operand layout used throughout (v_mfma_f32_32x32x16_bf16, lane l,
+// v = 0..7 for A/B, 0..15 for C):
+//   A[m][k]: m = l % 32, k = 8 (l / 32) + v
+//   B[k][n]: n = l % 32, k = 8 (l / 32) + v
+//   C[m][n]: m = 8 (v / 4) + 4 (l / 32) + v % 4, n = l % 32
+// Any permutation of k applied to both A and B leaves the product unchanged,
+// which the decode kernel uses to feed P straight from the score registers.
+//
+// ds_read_b64_tr_b16: within each 16-lane group, output lane j element e is
+// element (j % 4) of the 8 bytes addressed by source lane 4 e + j / 4.  With
+// source lane i addressing row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3 of a
+// row-major tile, lane j receives column c0 + j of rows r0 .. r0 + 3: a
+// K-strided operand fragment.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLn2 = 0.69314718055994530942f;
+// Lazy rescaling of the running softmax state: the reference maximum moves
+// only when a block's maximum exceeds it by more than this (log2 units), so
+// probabilities stay <= 2^8 and the accumulators are rescaled rarely.
+constexpr float kRescaleLog2 = 8.0f;
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr uint32_t kMaskedOffset = 0x80000000u; // beyond every record range: loads 0
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource: 48-bit base, stride 0, num_records bytes, 32-bit data
+// format.  Loads at offsets >= num_records return zeros.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = (int)kBufferFlags;
+  return r;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds, LDS base in M0).
+// Written as asm so that the compiler does not treat every later LDS read as
+// a possible alias of the in-flight load and wait for all of them; the
+// kernel orders these loads itself with s_waitcnt vmcnt and a barrier.  The
+// instruction has no destination register.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  i16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Two transpose reads (k-rows r and r + 4 of a fragment) joined into one
+// 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 tr_pair(const char LDS_AS* p0, const char LDS_AS* p1) {
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p0);
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)p1);
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Four floats -> four bf16 (round to nearest even), packed for an 8-byte store.
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
+  r.y = (uint32_t)bf16_bits(c) | ((uint32_t)bf16_bits(d) << 16);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// absorb: q_abs[b][h][c] = sum_d q_nope[b][h][d] W_UK,h[d][c]
+// Workgroup = (head, 128-column tile); wave w owns columns 32w .. 32w+31 and
+// loops over 32-row batch tiles.  W_UK is stored [d][c] (c contiguous) while
+// d is the reduction index, so the W tile is staged in LDS and read back with
+// transpose reads.  M = c (32), N = b (32), K = d (128).
+// ---------------------------------------------------------------------------
+constexpr int kAbsRowStride = 160;  // LDS row stride in elements (128 + 32 pad)
+
+__global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kNope * kAbsRowStride];
+  const int h = blockIdx.x >> 2, ctile = blockIdx.x & 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint16_t* w = a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ctile * 128;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int id = i * 256 + tid, row = id >> 4, cc = id & 15;
+    *reinterpret_cast<uint4*>(wt + row * kAbsRowStride + cc * 8) =
+        *reinterpret_cast<const uint4*>(w + (size_t)row * kLatent + cc * 8);
+  }
+  __syncthreads();
+
+  const int i16 = lane & 15, gm = (lane >> 4) & 1, hh = lane >> 5;
+  const char LDS_AS* wl = (const char LDS_AS*)wt;
+  bf16x8 af[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const int row0 = 16 * st + 8 * hh + (i16 >> 2);
+    const int col = wave * 32 + 16 * gm + 4 * (i16 & 3);
+    af[st] = tr_pair(wl + (row0 * kAbsRowStride + col) * 2, wl + ((row0 + 4) * kAbsRowStride + col) * 2);
+  }
+  for (int b0 = 0; b0 < a.B; b0 += 32) {
+    const int bb = b0 + (lane & 31);
+    const bool ok = bb < a.B;
+    const uint16_t* q = a.q_nope + (int64_t)(ok ? bb : 0) * a.q_sb + (int64_t)h * a.q_sh + 8 * hh;
+    f32x16 acc = {};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) acc = mfma32(af[st], ok ? ld8(q + 16 * st) : zero8(), acc);
+    if (ok) {
+      uint16_t* o = a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ctile * 128 + wave * 32 + 4 * hh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(o + 8 * q4) =
+            pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// value-up: out[b][h][d] = sum_c o_latent[b][h][c] W_UV,h[d][c]
+// One wave per (head, 32-row d tile): M = d, N = b, K = c (512).  Both
+// operands are contiguous along c, so they load straight from HBM; the W_UV
+// fragment (32 x 512) stays in registers across batch tiles.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void value_up_kernel(const ValueUpArgs a) {
+  const int h = blockIdx.x >> 2, dt = blockIdx.x & 3;
+  const int lane = threadIdx.x, hh = lane >> 5;
+  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + dt * 32 + (lane & 31)) * kLatent + 8 * hh;
+  bf16x8 wf[32];
+#pragma unroll
+  for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
+  for (int b0 = 0; b0 < a.B; b0 += 32) {
+    const int bb = b0 + (lane & 31);
+    const bool ok = bb < a.B;
+    const uint16_t* o = a.o_latent + ((int64_t)(ok ? bb : 0) * kHeads + h) * kLatent + 8 * hh;
+    f32x16 acc = {};
+#pragma unroll
+    for (int st = 0; st < 32; ++st) acc = mfma32(wf[st], ok ? ld8(o + 16 * st) : zero8(), acc);
+    if (ok) {
+      uint16_t* out = a.out + (int64_t)bb * a.out_sb + (int64_t)h * a.out_sh + dt * 32 + 4 * hh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(out + 8 * q4) =
+            pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode: sparse flash-decode over the selected cache rows.
+//
+// Workgroup = (sequence b, head group, key split); 4 waves.  With KL key lanes
+// (head_groups == KL), a workgroup covers 128 / KL heads as 4 / KL slices of
+// 32 heads; wave w = (slice w / KL, key lane w % KL).  Each block of
+// NKEY = 32 KL keys is gathered into LDS by buffer loads that write LDS
+// directly (16 bytes per lane, one 1 KiB line per instruction), NBUF blocks
+// in flight.  Masked slots get an offset past the record range, so their
+// rows arrive as zeros.
+//
+// LDS block layout: 16-byte slot (chunk c, key k) at c * NKEY + (k ^ sw(c)),
+// chunk c = 8 consecutive features of the 576-feature row [latent | rotary],
+// sw(c) = 8 ((c >> 1) & 1): rows are read contiguously by the score MFMA and
+// the transpose reads of the mix MFMA spread over all banks.
+//
+// Per wave and block of 32 keys:
+//   scores  S^T[key][head] = sum_f row[key][f] Q~[head][f]: A = rows (LDS,
+//           ds_read_b128), B = [q~ | q_pe] (registers), M = keys, N = heads,
+//           36 MFMAs over the 576 features.
+//   softmax each lane holds 16 keys of one head: in-lane max/sum plus one
+//           exchange with lane ^ 32; exp2 with the scale folded into log2 e.
+//   mix     O~^T[col][head] += sum_key C[key][col] P[head][key]: A = latent
+//           columns via transpose reads (M = 512 columns in 16 tiles), B = P
+//           taken from the score registers in place (K = keys, permuted
+//           consistently on both sides), N = heads.  Every accumulator of a
+//           lane belongs to its own head, so rescaling needs no exchange.
+// ---------------------------------------------------------------------------
+template <int KL, int NBUF, bool DENSE>
+__global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
+  constexpr int NKEY = 32 * KL;
+  constexpr int HPW = 128 / KL;                 // heads per workgroup
+  constexpr int BUF = 72 * NKEY * 16;           // bytes per block buffer
+  constexpr int GPW = BUF / 1024 / 4;           // gather instructions per wave per block
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF + kIdxCap * 4];
+  char LDS_AS* s3 = (char LDS_AS*)smem;
+  int* sidx = reinterpret_cast<int*>(smem + NBUF * BUF);
+
+  // Workgroup -> (sequence, split, head group).  Dispatch places workgroup i
+  // on XCD i % 8; the head groups of one (sequence, split) are given ids 8
+  // apart so they share an XCD (and its L2) and start together.
+  const int wg = blockIdx.x;
+  const int x8 = wg & 7, y = wg >> 3;
+  const int hg = y % KL;
+  const int unit = (y / KL) * 8 + x8;
+  if (unit >= a.B * a.S) return;
+  const int b = unit / a.S, s = unit % a.S;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = wave / KL, kl = wave % KL;
+  const int hh = lane >> 5;
+  const int head = hg * HPW + hs * 32 + (lane & 31);
+
+  constexpr bool dense = DENSE;
+  const bool validate = (a.flags & 1u) != 0 && hg == 0;
+  const int Lb = min(max(a.seq_lens[b], 0), a.max_len);
+  const int s0 = s * a.chunk;
+  const int s1 = min(a.k_max, s0 + a.chunk);
+  const int nslot = max(0, s1 - s0);
+  const int nblk = (nslot + NKEY - 1) / NKEY;
+
+  // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B layout.
+  bf16x8 qf[36];
+  {
+    const uint16_t* qa = a.q_abs + ((int64_t)b * kHeads + head) * kLatent + 8 * hh;
+#pragma unroll
+    for (int st = 0; st < 32; ++st) qf[st] = ld8(qa + 16 * st);
+    const uint16_t* qp = a.q_pe + (int64_t)b * a.q_pe_sb + (int64_t)head * a.q_pe_sh + 8 * hh;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qf[32 + st] = ld8(qp + 16 * st);
+  }
+
+  // Stage this split's index slots as cache rows (-1 = masked).  The same
+  // predicate decides validity, the attended bitmap and the device checks.
+  if constexpr (!dense) {
+    for (int i = tid; i < nblk * NKEY; i += 256) {
+      int row = -1;
+      if (i < nslot) {
+        const int t = a.indices[(int64_t)b * a.k_max + s0 + i];
+        const bool ok = t >= 0 && t < Lb;
+        row = ok ? t : -1;
+        if (validate) {
+          if (!ok && t != -1) atomicOr(a.status, 1u);
+          if (ok) {
+            const uint32_t bit = 1u << (t & 31);
+            const uint32_t old = atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), bit);
+            if (old & bit) atomicOr(a.status, 2u);
+          }
+        }
+      }
+      sidx[i] = row;
+    }
+  } else if (validate) {
+    for (int i = tid; i < nslot; i += 256) {
+      const int t = s0 + i;
+      if (t < Lb) atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), 1u << (t & 31));
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  auto row_of = [&](int i) -> int {  // slot i of this split -> cache row or -1
+    if constexpr (dense) {
+      const int t = s0 + i;
+      return (i < nslot && t < Lb) ? t : -1;
+    }
+    return sidx[i];
+  };
+
+  const uint32_t kv_rb = (uint32_t)(a.kv_st * 2), pe_rb = (uint32_t)(a.pe_st * 2);
+  const i32x4 rkv = buffer_rsrc(a.kv + (int64_t)b * a.kv_sb, (uint32_t)Lb * kv_rb);
+  const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)b * a.pe_sb, (uint32_t)Lb * pe_rb);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
+
+  // Gather block p into buffer p % NBUF.  A lane's slot in instruction g is
+  // g * 64 + lane; its key is (lane % NKEY) or that ^ 8, per sw(chunk).
+  auto issue = [&](int p) {
+    const int kA = lane & (NKEY - 1);
+    const int rA = row_of(p * NKEY + kA), rB = row_of(p * NKEY + (kA ^ 8));
+    const uint32_t okA = rA >= 0 ? (uint32_t)rA * kv_rb : kMaskedOffset;
+    const uint32_t okB = rB >= 0 ? (uint32_t)rB * kv_rb : kMaskedOffset;
+    const uint32_t opA = rA >= 0 ? (uint32_t)rA * pe_rb : kMaskedOffset;
+    const uint32_t opB = rB >= 0 ? (uint32_t)rB * pe_rb : kMaskedOffset;
+    const uint32_t dst = lds0 + (uint32_t)((p % NBUF) * BUF);
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int g = wave * GPW + i;
+      const int cb = (g * 64) / NKEY;            // chunk of lane 0 (uniform)
+      const int c = (g * 64 + lane) / NKEY;      // this lane's chunk
+      const bool useB = (cb >> 1) & 1;
+      const bool isPe = cb >= 64;
+      const uint32_t off = isPe ? (useB ? opB : opA) + (uint32_t)(c - 64) * 16
+                                : (useB ? okB : okA) + (uint32_t)c * 16;
+      dma16(isPe ? rpe : rkv, dst + (uint32_t)g * 1024, off);
+    }
+  };
+
+  f32x16 acc[16];
+#pragma unroll
+  for (int ct = 0; ct < 16; ++ct) acc[ct] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Per-lane LDS offsets.
+  const uint32_t qk_e = (uint32_t)((hh * NKEY + kl * 32 + (lane & 31)) * 16);
+  const uint32_t qk_o = (uint32_t)((hh * NKEY + kl * 32 + ((lane & 31) ^ 8)) * 16);
+  const int i16 = lane & 15, gm = (lane >> 4) & 1;
+  const uint32_t pc_base = (uint32_t)(((2 * gm + ((i16 & 3) >> 1)) * NKEY + kl * 32 + 4 * hh + (i16 >> 2)) * 16 + 8 * (i16 & 1));
+  const uint32_t pc_r0 = pc_base + gm * 128, pc_r1 = pc_base + (gm ^ 1) * 128;
+
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nblk) issue(p);
+
+  for (int j = 0; j < nblk; ++j) {
+    // Wait for block j: blocks j+1 .. j+NBUF-2 (when they exist) may stay in flight.
+    const int after = min(NBUF - 2, nblk - 1 - j);
+    if (NBUF >= 4 && after >= 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * GPW) : "memory");
+    } else if (NBUF >= 3 && after >= 1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GPW) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (j + NBUF - 1 < nblk) issue(j + NBUF - 1);
+
+    const char LDS_AS* buf = s3 + (j % NBUF) * BUF;
+
+    // Scores for this wave's 32 keys and 32 heads.  LDS reads run QK_AHEAD
+    // steps ahead of the MFMAs; the fences keep the scheduler from hoisting
+    // more (the query operand and the accumulators hold 400 registers).
+    f32x16 sacc = {};
+    {
+      constexpr int QK_AHEAD = 3;
+      bf16x8 ring[QK_AHEAD + 1];
+      auto qk_ld = [&](int st) {
+        const uint32_t off = ((st & 1) ? qk_o : qk_e) + (uint32_t)(st * 2 * NKEY * 16);
+        return *(const bf16x8 LDS_AS*)(buf + off);
+      };
+#pragma unroll
+      for (int st = 0; st < QK_AHEAD; ++st) ring[st] = qk_ld(st);
+#pragma unroll
+      for (int st = 0; st < 36; ++st) {
+        if (st + QK_AHEAD < 36) ring[(st + QK_AHEAD) % (QK_AHEAD + 1)] = qk_ld(st + QK_AHEAD);
+        sacc = mfma32(ring[st % (QK_AHEAD + 1)], qf[st], sacc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    const bool v_ok = row_of(j * NKEY + kl * 32 + (lane & 31)) >= 0;
+    const uint32_t vm = (uint32_t)__builtin_amdgcn_ballot_w64(v_ok);
+
+    float t[16];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
+      t[v] = ((vm >> kloc) & 1u) ? sacc[v] * a.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, t[v]);
+    }
+    if (a.flags & 2u) {
+      float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * NKEY + kl * 32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (j * NKEY + kl * 32 + kloc < nslot)
+          so[kloc] = ((vm >> kloc) & 1u) ? sacc[v] * a.scale : -INFINITY;
+      }
+    }
+    const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const bool need = mblk > m_run + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float mnew = need ? mblk : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+      l_run *= alpha;
+      // acc *= alpha, on the accumulator registers in place: a plain C++
+      // multiply would move all 256 accumulators into the VALU register file.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(acc[ct][v]), "=&v"(tmp)
+                       : "v"(alpha));
+        }
+      asm volatile("s_nop 3" ::: "memory");
+      m_run = mnew;
+    }
+    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 pb0, pb1;
+    float lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(t[v] - mref);
+      lsum += p;
+      if (v < 8) pb0[v] = (__bf16)p;
+      else pb1[v - 8] = (__bf16)p;
+    }
+    l_run += lsum;
+
+    // Mix the latents of this block into the accumulators (transpose reads
+    // PC_AHEAD MFMAs ahead, fenced as above).
+    {
+      constexpr int PC_AHEAD = 3;
+      bf16x8 ring[PC_AHEAD + 1];
+      auto pc_ld = [&](int i) {  // i = 2 ct + ks
+        const uint32_t o = (uint32_t)((i >> 1) * 4 * NKEY * 16 + (i & 1) * 256);
+        return tr_pair(buf + pc_r0 + o, buf + pc_r1 + o);
+      };
+#pragma unroll
+      for (int i = 0; i < PC_AHEAD; ++i) ring[i] = pc_ld(i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (i + PC_AHEAD < 32) ring[(i + PC_AHEAD) % (PC_AHEAD + 1)] = pc_ld(i + PC_AHEAD);
+        acc[i >> 1] = mfma32(ring[i % (PC_AHEAD + 1)], (i & 1) ? pb1 : pb0, acc[i >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+
+  if constexpr (KL == 2) {
+    // Merge the two key lanes of each head slice through LDS.
+    __syncthreads();
+    float* mrg = reinterpret_cast<float*>(smem) + hs * (16 * 16 * 64 + 128);
+    if (kl == 1) {
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mrg[(ct * 16 + v) * 64 + lane] = acc[ct][v];
+      mrg[16384 + lane] = m_run;
+      mrg[16384 + 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kl == 0) {
+      const float m2 = mrg[16384 + lane], l2 = mrg[16384 + 64 + lane];
+      const float M = fmaxf(m_run, m2);
+      const float a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+      l_run = l_run * a1 + l2 * a2;
+      m_run = M;
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ct][v] = acc[ct][v] * a1 + mrg[(ct * 16 + v) * 64 + lane] * a2;
+    }
+  }
+  if (kl != 0) return;
+
+  if (a.S == 1) {
+    const float inv = 1.0f / l_run;  // empty selection: 0 * inf = NaN
+    uint16_t* o = a.o_latent + ((int64_t)b * kHeads + head) * kLatent + 4 * hh;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(o + 32 * ct + 8 * q4) =
+            pack4(acc[ct][4 * q4] * inv, acc[ct][4 * q4 + 1] * inv, acc[ct][4 * q4 + 2] * inv,
+                  acc[ct][4 * q4 + 3] * inv);
+    if (a.lse != nullptr && hh == 0)
+      a.lse[(int64_t)b * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    if (validate && hs == 0 && lane == 0 && !(l_run > 0.f)) atomicOr(a.status, 4u);
+  } else {
+    float* pa = a.part_acc + (((int64_t)s * a.B + b) * kHeads + head) * kLatent + 4 * hh;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(pa + 32 * ct + 8 * q4) =
+            f32x4{acc[ct][4 * q4], acc[ct][4 * q4 + 1], acc[ct][4 * q4 + 2], acc[ct][4 * q4 + 3]};
+    if (hh == 0) {
+      float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + head) * 2;
+      pml[0] = m_run;
+      pml[1] = l_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: O~ = sum_s w_s acc_s / sum_s w_s l_s, w_s = 2^(m_s - max m)
+// Workgroup = (sequence, 2 heads); each thread owns 4 latent columns.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+  const int b = blockIdx.x >> 6;
+  const int head = (blockIdx.x & 63) * 2 + (threadIdx.x >> 7);
+  const int col = (threadIdx.x & 127) * 4;
+  const int64_t stride_s = (int64_t)a.B * kHeads;
+  const int64_t bh = (int64_t)b * kHeads + head;
+  float M = -INFINITY;
+  for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[(s * stride_s + bh) * 2]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.S; ++s) {
+    const float ms = a.part_ml[(s * stride_s + bh) * 2];
+    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L += w * a.part_ml[(s * stride_s + bh) * 2 + 1];
+    acc += w * *reinterpret_cast<const f32x4*>(a.part_acc + (s * stride_s + bh) * kLatent + col);
+  }
+  const float inv = 1.0f / L;
+  *reinterpret_cast<uint2*>(a.o_latent + bh * kLatent + col) =
+      pack4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if ((threadIdx.x & 127) == 0) {
+    if (a.lse != nullptr) a.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    if (a.status != nullptr && head == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 dequantisation (one-time set-up).  E4M3FN from its definition: sign,
+// 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal
+// (m/8 * 2^-6); 0x7F / 0xFF are NaN.  The product with the fp32 block scale
+// is rounded to bf16 from its exact value: p = fl(v * s) plus the exact
+// residual fma(v, s, -p) decide the rare ties that fl() creates.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  float v;
+  if (e == 0u) v = (float)m * 0x1p-9f;
+  else if (e == 15u && m == 7u) v = __builtin_nanf("");
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (code & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_exact(float p, float err) {
+  const uint32_t u = __float_as_uint(p);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  const uint32_t lower = u & 0xffffu, hi = u >> 16;
+  bool up;
+  if (lower > 0x8000u) up = true;
+  else if (lower < 0x8000u) up = false;
+  else if (err == 0.f) up = (hi & 1u) != 0u;
+  else up = (err > 0.f) == (p > 0.f);   // the exact value lies beyond the tie
+  return hi + (up ? 1u : 0u);
+}
+
+__global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int row = (int)(i / kLatent), col = (int)(i % kLatent);
+  const float sc = a.scales[(row / 128) * (kLatent / 128) + col / 128];
+  const uint2 codes = *reinterpret_cast<const uint2*>(a.w + i);
+  uint32_t outw[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t word = (e + k) < 4 ? codes.x : codes.y;
+      const uint32_t code = (word >> (8 * ((e + k) & 3))) & 0xffu;
+      const float v = e4m3_value(code);
+      const float p = v * sc;
+      const float err = __builtin_fmaf(v, sc, -p);
+      pair |= bf16_rne_exact(p, err) << (16 * k);
+    }
+    outw[e / 2] = pair;
+  }
+  *reinterpret_cast<uint4*>(a.out + i) = uint4{outw[0], outw[1], outw[2], outw[3]};
+}
+
+}  // namespace
+
+int launch_absorb(const AbsorbArgs& a, void* stream) {
+  hipLaunchKernelGGL(absorb_kernel, dim3(kHeads * 4), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_decode(const DecodeArgs& a, int head_groups, void* stream) {
+  const int units = a.B * a.S;
+  const int groups8 = (units + 7) / 8;
+  const hipStream_t st = (hipStream_t)stream;
+  const bool dense = a.indices == nullptr;
+  if (head_groups == 2) {
+    if (dense) hipLaunchKernelGGL((decode_kernel<2, 2, true>), dim3(groups8 * 16), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<2, 2, false>), dim3(groups8 * 16), dim3(256), 0, st, a);
+  } else {
+    if (dense) hipLaunchKernelGGL((decode_kernel<1, 4, true>), dim3(groups8 * 8), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((decode_kernel<1, 4, false>), dim3(groups8 * 8), dim3(256), 0, st, a);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_combine(const CombineArgs& a, void* stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_value_up(const ValueUpArgs& a, void* stream) {
+  hipLaunchKernelGGL(value_up_kernel, dim3(kHeads * 4), dim3(64), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_dequant(const DequantArgs& a, void* stream) {
+  const size_t n = (size_t)kHeads * kRowsPerHead * kLatent;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)(n / 8 / 256)), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int device_cu_count(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+}  // namespace mla

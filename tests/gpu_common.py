@@ -1,0 +1,54 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_mla_amd import workload
+
+# the benchmark spec tolerance: max |O - O_ref| <= 1e-2 * max |O_ref| (the same bar is
+# used for the absorbed query and the latent mix); softmax rows sum to one
+# within 1e-3.
+REL_TOL = 1e-2
+ROWSUM_TOL = 1e-3
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+def to_gpu(w: workload.Workload) -> workload.Workload:
+    dev = "cuda"
+    mv = lambda t: None if t is None else t.to(dev)  # noqa: E731
+    return workload.Workload(spec=w.spec, B=w.B, seq_lens=mv(w.seq_lens), max_len=w.max_len,
+                             q_nope=mv(w.q_nope), q_pe=mv(w.q_pe), cache=mv(w.cache),
+                             wkv_b=mv(w.wkv_b), indices=mv(w.indices), wkv_b_fp8=mv(w.wkv_b_fp8),
+                             wkv_b_scale=mv(w.wkv_b_scale), scale=w.scale)
+
+
+def oracle_ref(w: workload.Workload, rows=None, want_weights=False):
+    """Oracle outputs for sequences ``rows`` (default all) of a CPU-side workload."""
+    rows = list(range(w.B)) if rows is None else list(rows)
+    sel = torch.tensor(rows)
+    idx = None if w.indices is None else w.indices.cpu()[sel].to(torch.int64)
+    if idx is None and want_weights:
+        idx = torch.stack([torch.cat([torch.arange(int(w.seq_lens[r])),
+                                      torch.full((w.max_len - int(w.seq_lens[r]),), -1)]) for r in rows])
+    cache = w.cache.cpu()[sel]
+    return oracle.decode(w.q_nope.cpu()[sel], w.q_pe.cpu()[sel], cache[..., :workload.DC],
+                         cache[..., workload.DC:], w.wkv_b.cpu(), w.seq_lens.cpu()[sel], idx, w.scale,
+                         want_weights=want_weights, want_attended=True, att_len=cache.shape[1])
+
+
+def rowsum_dev(ref_scores: np.ndarray, lse_gpu: np.ndarray) -> float:
+    """max over (b,h) of |sum_t exp(s_ref[t] - LSE_gpu) - 1| over the selected slots
+    (masked slots carry -inf and contribute 0)."""
+    s = np.exp(ref_scores - lse_gpu[..., None])
+    return float(np.max(np.abs(s.sum(-1) - 1.0)))

@@ -1,0 +1,163 @@
+"""GPU parity of every HIP kernel against the CPU oracle on small seeded
+inputs that span several tiles and a ragged tail (called through the C ABI
+via sparse_mla_amd.binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_amd import workload
+from tests.gpu_common import REL_TOL, ROWSUM_TOL, f64, oracle_ref, rel_err, rowsum_dev, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_mla_amd import binding
+    return binding
+
+
+def test_absorb_q(mla):
+    w = workload.make("sparse_b32_l4096_k2048", B=37, L=8, k=4)   # two batch tiles, ragged
+    g = to_gpu(w)
+    q_abs = mla.mla_absorb_q(g.q_nope, g.wkv_b)
+    torch.cuda.synchronize()
+    ref = oracle.absorb(w.q_nope, w.wkv_b)
+    assert rel_err(f64(q_abs), ref) <= 4e-3
+
+
+def test_absorb_q_strided_query(mla):
+    """q_nope as the first 128 columns of a [B,1,128,192] query tensor."""
+    B = 5
+    q = torch.randn((B, 1, 128, 192), generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    w = workload.make("sparse_b32_l4096_k2048", B=1, L=8, k=4)
+    q_abs = mla.mla_absorb_q(q.cuda()[..., :128], w.wkv_b.cuda())
+    torch.cuda.synchronize()
+    assert rel_err(f64(q_abs), oracle.absorb(q[..., :128], w.wkv_b)) <= 4e-3
+
+
+def test_value_up(mla):
+    B = 45
+    gen = torch.Generator().manual_seed(11)
+    o_lat = torch.randn((B, 128, 512), generator=gen).to(torch.bfloat16)
+    w = workload.make("sparse_b32_l4096_k2048", B=1, L=8, k=4)
+    out = mla.mla_value_up(o_lat.cuda(), w.wkv_b.cuda())
+    torch.cuda.synchronize()
+    assert rel_err(f64(out)[:, 0], oracle.value_up(o_lat, w.wkv_b)) <= 4e-3
+
+
+def _run_decode(mla, g, S, HG, layout="packed", flags=0, bitmap=None, scores=None, status=None):
+    B = g.B
+    k_max = g.k_max
+    bufs = mla.DecodeBuffers.allocate(B, k_max, g.indices is None, num_splits=S, head_groups=HG)
+    if layout == "packed":
+        kv, pe = g.kv, g.pe
+    else:  # two buffers, as in the pages' code
+        kv, pe = g.kv.contiguous(), g.pe.contiguous()
+    out = mla.decode_step(bufs, g.q_nope, g.q_pe, kv, pe, g.wkv_b, g.seq_lens, g.max_len, g.indices,
+                          g.scale, flags=flags, bitmap=bitmap, scores=scores, status=status)
+    torch.cuda.synchronize()
+    return bufs, out
+
+
+CASES = [
+    # (name, B, L, k, S, HG, layout)
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 1, 1, "packed"),
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 1, 2, "packed"),
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 3, 2, "packed"),
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 2, 1, "split"),
+    ("longctx_b64_k2048", 4, 3000, 700, 1, 1, "packed"),
+    ("longctx_b64_k2048", 4, 3000, 700, 2, 2, "split"),
+    ("longctx_b64_k2048", 4, 3000, 700, 5, 1, "packed"),
+    ("dense_p1000_b1", 2, 1001, None, 1, 2, "packed"),
+    ("dense_p1000_b1", 2, 1001, None, 4, 1, "split"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-B{c[1]}-L{c[2]}-k{c[3]}-S{c[4]}-HG{c[5]}-{c[6]}")
+def test_decode_small(mla, case):
+    name, B, L, k, S, HG, layout = case
+    w = workload.make(name, B=B, L=L, k=k)
+    if w.indices is not None:
+        w.indices[0, -7:] = -1          # padding slots in one row
+    g = to_gpu(w)
+    bufs, out = _run_decode(mla, g, S, HG, layout)
+    ref = oracle_ref(w, want_weights=True)
+    assert rel_err(f64(bufs.o_latent), ref["o_lat"]) <= REL_TOL
+    assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
+    assert rowsum_dev(ref["scores"], f64(bufs.lse)) <= ROWSUM_TOL
+
+
+def test_decode_validate_bitmap_and_scores(mla):
+    """VALIDATE: the attended bitmap equals the oracle's set bit for bit;
+    WRITE_SCORES: the kernel's own scores normalise against its LSE."""
+    w = workload.make("longctx_b64_k2048", B=3, L=2500, k=300)
+    w.indices[1, 10:20] = -1
+    g = to_gpu(w)
+    words = (w.max_len + 31) // 32
+    bitmap = torch.zeros((w.B, words), dtype=torch.int32, device="cuda")
+    scores = torch.empty((w.B, 128, w.k_max), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs, out = _run_decode(mla, g, 2, 2, flags=mla.MLA_FLAG_VALIDATE | mla.MLA_FLAG_WRITE_SCORES,
+                            bitmap=bitmap, scores=scores, status=status)
+    assert int(status.item()) == 0
+    ref = oracle_ref(w, want_weights=True)
+    bits = bitmap.cpu().numpy().view(np.uint32)
+    got = np.zeros((w.B, words * 32), dtype=np.uint8)
+    for t in range(32):
+        got[:, t::32] = (bits >> t) & 1
+    att = ref["attended"]
+    n = min(att.shape[1], got.shape[1])
+    assert np.array_equal(got[:, :n], att[:, :n])
+    assert not got[:, n:].any() and not att[:, n:].any()
+    sc = f64(scores)
+    ref_sc = ref["scores"]
+    masked = np.isneginf(ref_sc)
+    assert np.array_equal(np.isneginf(sc), masked)
+    assert np.max(np.abs(sc[~masked] - ref_sc[~masked])) <= 2e-2
+    assert rowsum_dev(sc, f64(bufs.lse)) <= ROWSUM_TOL
+
+
+@pytest.mark.parametrize("S,HG", [(1, 1), (2, 2)])
+def test_decode_validate_errors(mla, S, HG):
+    """Out-of-range and repeated indices and an empty row set the status
+    bits; the empty sequence yields NaN and the others stay finite."""
+    w = workload.make("sparse_b32_l4096_k2048", B=3, L=200, k=64)
+    w.indices[0, 3] = 500            # out of range (L = 200)
+    w.indices[1, 5] = w.indices[1, 6]  # duplicate
+    w.indices[2, :] = -1             # empty selection
+    g = to_gpu(w)
+    bitmap = torch.zeros((w.B, 8), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs, out = _run_decode(mla, g, S, HG, flags=mla.MLA_FLAG_VALIDATE, bitmap=bitmap, status=status)
+    st = int(status.item())
+    assert st == (mla.MLA_DEV_INDEX_OUT_OF_RANGE | mla.MLA_DEV_DUPLICATE_INDEX | mla.MLA_DEV_EMPTY_SELECTION)
+    o = f64(out)
+    assert np.all(np.isnan(o[2])) and np.all(np.isfinite(o[:2]))
+    assert np.all(np.isneginf(f64(bufs.lse)[2]))
+
+
+def test_dequant_fp8_bit_exact(mla):
+    codes, scales = workload.fp8_weights(128 * 256, 512, seed=5000)
+    bits, _ = oracle.dequant_fp8(codes, scales)
+    out = mla.mla_dequant_wkv_b_fp8(codes.cuda(), scales.cuda())
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, bits)
+
+
+def test_decode_deterministic_and_order_invariant(mla):
+    w = workload.make("sparse_b32_l4096_k2048", B=4, L=1000, k=256)
+    g = to_gpu(w)
+    _, out1 = _run_decode(mla, g, 2, 2)
+    o1 = out1.clone()
+    _, out2 = _run_decode(mla, g, 2, 2)
+    assert torch.equal(o1, out2)
+    perm = torch.randperm(w.k_max, generator=torch.Generator().manual_seed(3))
+    g.indices = g.indices[:, perm.cuda()].contiguous()
+    _, out3 = _run_decode(mla, g, 2, 2)
+    ref = oracle_ref(w)
+    assert rel_err(f64(out3)[:, 0], ref["out"]) <= REL_TOL

@@ -107,3 +107,31 @@ def test_dequant_fp8_exact():
         v = Fraction(oracle.e4m3_to_double(int(codes[i, j]))) * Fraction(float(scales[i // 128, j // 128]))
         assert Fraction(exact[i, j]) == v
         assert bits[i, j] == _bf16_exact_rne(float(v)) or v == 0
+
+
+def test_step_absorb_identity_and_agreement():
+    """oracle.absorb: W_UK = [I | 0] gives [q_nope, 0] exactly, and it equals
+    the absorbed query the full oracle reports."""
+    x = pins.make_inputs(30, 2, 6, 3, **pins.REAL)
+    full = oracle.decode(**x)
+    assert np.array_equal(oracle.absorb(x["q_nope"], x["wkv_b"]), full["q_abs"])
+    H, Dn, Dc, Dv = 128, 128, 512, 128
+    w = x["wkv_b"].reshape(H, Dn + Dv, Dc).copy()
+    w[:, :Dn, :] = 0.0
+    w[:, np.arange(Dn), np.arange(Dn)] = 1.0
+    got = oracle.absorb(x["q_nope"], w.reshape(-1, Dc))
+    assert np.array_equal(got[:, :, :Dn], x["q_nope"]) and np.all(got[:, :, Dn:] == 0.0)
+
+
+def test_step_value_up_identity_and_agreement():
+    """oracle.value_up: W_UV = [I | 0] gives the first 128 latent features
+    exactly, and it equals the output the full oracle reports."""
+    x = pins.make_inputs(31, 2, 6, 3, **pins.REAL)
+    full = oracle.decode(**x)
+    assert np.array_equal(oracle.value_up(full["o_lat"], x["wkv_b"]), full["out"])
+    H, Dn, Dc, Dv = 128, 128, 512, 128
+    w = x["wkv_b"].reshape(H, Dn + Dv, Dc).copy()
+    w[:, Dn:, :] = 0.0
+    w[:, Dn + np.arange(Dv), np.arange(Dv)] = 1.0
+    o = np.random.default_rng(1).standard_normal((2, H, Dc))
+    assert np.array_equal(oracle.value_up(o, w.reshape(-1, Dc)), o[:, :, :Dv])
