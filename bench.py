@@ -1,0 +1,281 @@
+"""Benchmark of the absorbed sparse MLA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload NAME]
+
+One step = mla_absorb_q + mla_sparse_decode + (mla_combine + mla_value_up, as
+the single fused mla_combine_value_up launch when the plan splits the keys)
+over a batch of B single-token queries, all inputs resident in HBM.  Input sets are
+rotated (distinct index sets, queries and weight copies; whole caches when they
+are small) so that every cycle moves >= 1 GB and the 256 MB memory-side cache
+cannot serve a repeated step.  Prints ONE JSON line.
+
+The roofline entry is for the dominant kernel (the sparse decode): its
+algorithmic bytes per launch (selected cache rows at 1152 B + 4 B per index)
+over its mean launch time, timed with HIP events on the launch stream.
+The CPU baseline runs the fp64 oracle (oracle/, test infrastructure) on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+ROW_BYTES = 1152               # 512 latent + 64 rotary bf16 values per position
+FLOP_PER_KEY = 2 * 128 * (576 + 512)
+WEIGHT_BYTES = 2 * 128 * 128 * 512 * 2   # W_UK and W_UV, bf16
+Q_BYTES_PER_QUERY = 128 * (128 + 64) * 2
+O_BYTES_PER_QUERY = 128 * 128 * 2
+METRIC = "sparse MLA decode queries/s at B=64,k=2048; % of HBM/MFMA roofline"
+ROTATION = {"dense_p1000_b1": 32, "sparse_b32_l4096_k2048": 10, "longctx_b64_k2048": 6,
+            "verylong_b128_l131072_k2048": 3, "dense_fp8w_b64_l8192": 2}
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the B=64, k=2048 long-context case)")
+    ap.add_argument("--rotate", type=int, default=None, help="input sets cycled through (default per workload)")
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--head-groups", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="sequences in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": {"read": n, "write": n}, "launches": 5}))
+
+
+def make_sets(name, R, torch, workload):
+    """R input sets of one workload.  Large caches are shared and only the
+    index sets, queries and weights rotate; small caches rotate too."""
+    spec = workload.SPECS[name]
+    cache_bytes = spec.B * spec.L * ROW_BYTES
+    base = workload.make(name, device="cpu", cache_device="cuda")
+    sets = []
+    for v in range(R):
+        if v == 0:
+            w = base
+        else:
+            shared = base.cache if cache_bytes > (1 << 28) else None
+            w = workload.make(name, device="cpu", cache_device="cuda", variant=v, lens=base.seq_lens.cpu(),
+                              cache=shared)
+        dev = {}
+        for key in ("q_nope", "q_pe", "wkv_b", "indices", "wkv_b_fp8", "wkv_b_scale", "seq_lens"):
+            t = getattr(w, key)
+            dev[key] = None if t is None else t.to("cuda")
+        w.q_nope, w.q_pe, w.wkv_b, w.indices = dev["q_nope"], dev["q_pe"], dev["wkv_b"], dev["indices"]
+        w.wkv_b_fp8, w.wkv_b_scale, w.seq_lens = dev["wkv_b_fp8"], dev["wkv_b_scale"], dev["seq_lens"]
+        sets.append(w)
+    return sets
+
+
+def cpu_baseline(w, n_seq, torch, workload):
+    """The fp64 oracle on the first n_seq sequences of input set 0: selected
+    rows are gathered to the host (marshalling, untimed), the oracle call is
+    timed."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    rows = list(range(n_seq))
+    kvs, pes, idxs, lens = [], [], [], []
+    for b in rows:
+        Lb = int(w.seq_lens[b])
+        if w.indices is None:
+            pos = torch.arange(Lb, device="cuda")
+        else:
+            pos = w.indices[b].long()
+            pos = pos[pos >= 0]
+        r = w.cache[b].index_select(0, pos).cpu()
+        kvs.append(r[:, : workload.DC])
+        pes.append(r[:, workload.DC:])
+        lens.append(r.shape[0])
+    k = max(lens)
+    kv = torch.zeros((n_seq, k, workload.DC), dtype=torch.bfloat16)
+    pe = torch.zeros((n_seq, k, workload.DR), dtype=torch.bfloat16)
+    for i in range(n_seq):
+        kv[i, : lens[i]] = kvs[i]
+        pe[i, : lens[i]] = pes[i]
+    seq = torch.tensor(lens, dtype=torch.int32)
+    wkv = w.wkv_b.cpu()
+    qn = w.q_nope[:n_seq].cpu()
+    qp = w.q_pe[:n_seq].cpu()
+    t0 = time.perf_counter()
+    res = oracle.decode(qn, qp, kv, pe, wkv, seq, None, w.scale)
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return res, dt, threads, np
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
+
+    from sparse_mla_amd import binding as mla
+    from sparse_mla_amd import workload
+
+    name = args.workload or workload.HEADLINE
+    spec = workload.SPECS[name]
+    R = args.rotate or ROTATION[name]
+    log(f"workload {name}: {spec.description}; {R} rotating input sets")
+    t0 = time.perf_counter()
+    sets = make_sets(name, R, torch, workload)
+    if spec.fp8:  # one-time set-up, untimed: dequantise each weight copy once
+        for w in sets:
+            w.wkv_b = mla.mla_dequant_wkv_b_fp8(w.wkv_b_fp8, w.wkv_b_scale)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s")
+
+    w0 = sets[0]
+    B = w0.B
+    dense = w0.indices is None
+    k_max = w0.k_max
+    bufs = mla.DecodeBuffers.allocate(B, k_max, dense, num_splits=args.splits, head_groups=args.head_groups)
+    stream = torch.cuda.current_stream()
+
+    def step(w, ev=None):
+        mla.mla_absorb_q(w.q_nope, w.wkv_b, bufs.q_abs)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_sparse_decode(bufs.q_abs, w.q_pe, w.kv, w.pe, w.seq_lens, w.max_len, w.indices, w.scale,
+                              bufs.num_splits, bufs.head_groups, bufs.workspace, bufs.o_latent, bufs.lse,
+                              k_max=k_max)
+        if ev is not None:
+            ev[1].record(stream)
+        if bufs.num_splits > 1:
+            mla.mla_combine_value_up(bufs.workspace, B, bufs.num_splits, w.wkv_b, bufs.out, lse=bufs.lse)
+        else:
+            mla.mla_value_up(bufs.o_latent, w.wkv_b, bufs.out)
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(sets[i % R], evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    decode_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    log(f"{args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us), "
+        f"decode kernel {decode_ms * 1e3:.2f} us; plan splits={bufs.num_splits} head_groups={bufs.head_groups}")
+
+    # Algorithmic work.
+    if dense:
+        keys = int(w0.seq_lens.sum().item())
+        idx_bytes = 0
+    else:
+        keys = int((w0.indices >= 0).sum().item())
+        idx_bytes = 4 * keys
+    dec_bytes = keys * ROW_BYTES + idx_bytes
+    dec_flops = keys * FLOP_PER_KEY
+    step_bytes = dec_bytes + WEIGHT_BYTES + B * (Q_BYTES_PER_QUERY + O_BYTES_PER_QUERY)
+    step_flops = dec_flops + B * 2 * (2 * 128 * 128 * 512)
+    dec_gbs = dec_bytes / (decode_ms * 1e-3) / 1e9
+    dec_tflops = dec_flops / (decode_ms * 1e-3) / 1e12
+    step_roof_s = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (BF16_PEAK_TFLOPS * 1e12))
+
+    # Sampled parity of the timed output (last step's input set) against the oracle.
+    parity = None
+    try:
+        import numpy as np
+
+        import oracle
+        last = sets[(args.steps - 1) % R]
+        b = 0
+        Lb = int(last.seq_lens[b])
+        pos = torch.arange(Lb, device="cuda") if dense else last.indices[b].long()
+        pos = pos[pos >= 0]
+        rows = last.cache[b].index_select(0, pos).cpu()[None]
+        ref = oracle.decode(last.q_nope[:1].cpu(), last.q_pe[:1].cpu(), rows[..., : workload.DC],
+                            rows[..., workload.DC:], last.wkv_b.cpu(), torch.tensor([rows.shape[1]]), None,
+                            last.scale)["out"][0]
+        got = bufs.out[0, 0].float().cpu().numpy()
+        parity = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        log(f"sampled parity (sequence 0): max|O-O_ref|/max|O_ref| = {parity:.2e}")
+    except Exception as e:  # noqa: BLE001 - report, do not hide the measurement
+        log(f"sampled parity check skipped: {e!r}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_seq = args.cpu_sample or {"dense_p1000_b1": 1, "sparse_b32_l4096_k2048": 32, "longctx_b64_k2048": 64,
+                                    "verylong_b128_l131072_k2048": 64, "dense_fp8w_b64_l8192": 8}[name]
+        log(f"oracle CPU baseline on {n_seq} sequences ...")
+        _, dt, threads, _ = cpu_baseline(w0, n_seq, torch, workload)
+        cpu = {"value": n_seq / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n_seq} of {B} sequences of input set 0 (all 128 heads, all their selected "
+                         f"positions), fp64 C oracle with OpenMP, {dt:.2f} s wall"}
+        log(f"oracle: {dt:.2f} s for {n_seq} queries on {threads} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": B / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "B": B, "k_max": k_max, "selected_keys": keys,
+            "cache": f"[{B}, {spec.L}, 576] bf16 packed rows", "rotating_sets": R,
+            "num_splits": bufs.num_splits, "head_groups": bufs.head_groups,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "mla_sparse_decode", "kernel_us": decode_ms * 1e3,
+            "bytes_per_launch": dec_bytes, "mfma_tflops": dec_tflops,
+            "mfma_frac": dec_tflops / BF16_PEAK_TFLOPS,
+        },
+        "step_roofline_frac": step_roof_s / (ms_step * 1e-3),
+        "parity_sampled_rel_err": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -95,8 +95,9 @@ int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus,
 /*
  * Bytes of workspace mla_sparse_decode needs for `num_splits` splits: 0 when
  * num_splits == 1 (the normalised result is written directly), otherwise the
- * fp32 partial mixes [S][B][128][512] and the per-head (max, sum) pairs
- * [S][B][128][2].  Returns 0 for invalid arguments.
+ * per-split normalised latent mixes, bf16 [S][B][128][512], followed by the
+ * per-split (max in log2 units, sum) pairs, fp32 [S][B][128][2].
+ * Returns 0 for invalid arguments.
  */
 size_t mla_workspace_bytes(int32_t B, int32_t num_splits);
 
@@ -181,6 +182,17 @@ int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_s
  */
 int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
                  int64_t out_sb, int64_t out_sh, int32_t B, void* stream);
+
+/*
+ * Steps 3 and 4 in one launch, for num_splits >= 2: the value-up of step 4
+ * reads its O~ operand merged on the fly from the split partials in
+ * `workspace` (the same merge as mla_combine), so O~ is never stored.
+ * out as in mla_value_up; lse fp32 [B][128] (may be NULL); status_dev as in
+ * mla_combine (may be NULL).
+ */
+int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                         const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh, float* lse,
+                         uint32_t* status_dev, void* stream);
 
 /*
  * One-time set-up ("Query-key similarity" page, code excerpt: a quantised

@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+# MLA_DECODE_LIB selects another build of the same library (e.g. a debug build).
+LIB_PATH = os.environ.get("MLA_DECODE_LIB", os.path.join(_HERE, "libmla_decode.so"))
 
 MLA_FLAG_VALIDATE = 1
 MLA_FLAG_WRITE_SCORES = 2
@@ -59,6 +60,8 @@ _decode = _sig("mla_sparse_decode", ctypes.c_int, [
 ])
 _combine = _sig("mla_combine", ctypes.c_int, [_p, _sz, _i32, _i32, _p, _p, _p, _p])
 _value_up = _sig("mla_value_up", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p])
+_combine_value_up = _sig("mla_combine_value_up", ctypes.c_int,
+                         [_p, _sz, _i32, _i32, _p, _p, _i64, _i64, _p, _p, _p])
 _dequant = _sig("mla_dequant_wkv_b_fp8", ctypes.c_int, [_p, _p, _p, _p])
 
 
@@ -205,6 +208,21 @@ def mla_value_up(o_latent: torch.Tensor, wkv_b: torch.Tensor, out: Optional[torc
     return out
 
 
+def mla_combine_value_up(workspace, B: int, num_splits: int, wkv_b: torch.Tensor,
+                         out: Optional[torch.Tensor] = None, lse=None, status=None, stream=None) -> torch.Tensor:
+    _need(wkv_b, "wkv_b", torch.bfloat16, 2)
+    if out is None:
+        out = torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=wkv_b.device)
+    _need(out, "out", torch.bfloat16)
+    Bo, Ho, sb, sh = _bsh(out)
+    if Bo != B or Ho != HEADS or out.shape[-1] != VALUE:
+        raise ValueError("out must be [B,1,128,128] or [B,128,128]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_combine_value_up", _combine_value_up(_ptr(workspace), ws_bytes, B, num_splits, _ptr(wkv_b),
+                                                     _ptr(out), sb, sh, _ptr(lse), _ptr(status), _stream(stream)))
+    return out
+
+
 def mla_dequant_wkv_b_fp8(w_fp8: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None,
                           stream=None) -> torch.Tensor:
     _need(w_fp8, "w_fp8", torch.uint8, 2)
@@ -245,18 +263,25 @@ class DecodeBuffers:
             o_latent=torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=device),
             lse=torch.empty((B, HEADS), dtype=torch.float32, device=device),
             out=torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=device),
-            workspace=torch.empty(ws // 4, dtype=torch.float32, device=device) if ws else None,
+            workspace=torch.empty(ws, dtype=torch.uint8, device=device) if ws else None,
         )
 
 
 def decode_step(bufs: DecodeBuffers, q_nope, q_pe, kv, pe, wkv_b, seq_lens, max_len, indices, scale,
-                flags=0, bitmap=None, scores=None, status=None, stream=None) -> torch.Tensor:
-    """The four calls of one decode step, enqueued on one stream."""
+                flags=0, bitmap=None, scores=None, status=None, stream=None, fused=True) -> torch.Tensor:
+    """One decode step enqueued on one stream: absorb, sparse decode, then
+    combine + value-up (one fused launch when there are splits and ``fused``;
+    with fused, bufs.o_latent is not written when num_splits > 1)."""
     mla_absorb_q(q_nope, wkv_b, bufs.q_abs, stream=stream)
     mla_sparse_decode(bufs.q_abs, q_pe, kv, pe, seq_lens, max_len, indices, scale,
                       bufs.num_splits, bufs.head_groups, bufs.workspace, bufs.o_latent, bufs.lse,
                       flags=flags, bitmap=bitmap, scores=scores, status=status,
                       k_max=bufs.k_max, stream=stream)
-    mla_combine(bufs.workspace, bufs.B, bufs.num_splits, bufs.o_latent, bufs.lse, status=status, stream=stream)
-    mla_value_up(bufs.o_latent, wkv_b, bufs.out, stream=stream)
+    if bufs.num_splits > 1 and fused:
+        mla_combine_value_up(bufs.workspace, bufs.B, bufs.num_splits, wkv_b, bufs.out, lse=bufs.lse,
+                             status=status, stream=stream)
+    else:
+        mla_combine(bufs.workspace, bufs.B, bufs.num_splits, bufs.o_latent, bufs.lse, status=status,
+                    stream=stream)
+        mla_value_up(bufs.o_latent, wkv_b, bufs.out, stream=stream)
     return bufs.out

@@ -58,15 +58,15 @@ size_t mla_workspace_bytes(int32_t B, int32_t num_splits) {
   if (B < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
   if (num_splits == 1) return 0;
   const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
-  return units * MLA_LATENT_DIM * sizeof(float) + units * 2 * sizeof(float);
+  return units * MLA_LATENT_DIM * sizeof(uint16_t) + units * 2 * sizeof(float);
 }
 
 // Cost model (in nanoseconds) over head groups {1, 2} and splits 1..64:
 //  * compute: rounds of workgroups over the CUs times the keys each wave
 //    walks (a head-group-2 workgroup gives each wave half of its keys), at
 //    ~45 ns per key per wave (68 MFMA of 32x32x16 per 32 keys, ~60% busy);
-//  * partials: every extra split writes and re-reads a 128 x 512 fp32 mix
-//    per sequence, at ~5 TB/s, plus a combine launch.
+//  * partials: every extra split writes and re-reads a 128 x 512 bf16 mix
+//    per sequence, at ~5 TB/s.
 // Sparse mode caps a split at MLA_MAX_SLOTS_PER_SPLIT slots.
 int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus,
              int32_t* num_splits, int32_t* head_groups) {
@@ -82,7 +82,7 @@ int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus,
       const int64_t wgs = (int64_t)B * S * hg;
       const int64_t rounds = ceil_div(wgs, num_cus);
       const double t_compute = (double)rounds * (double)(chunk / hg) * 45.0;
-      const double t_part = S > 1 ? (double)S * B * MLA_HEADS * MLA_LATENT_DIM * 4.0 * 2.0 / 5.0e3 + 3000.0 : 0.0;
+      const double t_part = S > 1 ? (double)S * B * MLA_HEADS * MLA_LATENT_DIM * 2.0 * 2.0 / 5.0e3 : 0.0;
       const double t = t_compute + t_part;
       if (t < best * 0.999) {
         best = t;
@@ -175,8 +175,10 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
-  a.part_acc = num_splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  a.part_ml = num_splits > 1 ? static_cast<float*>(workspace) + units * MLA_LATENT_DIM : nullptr;
+  a.part_o = num_splits > 1 ? static_cast<uint16_t*>(workspace) : nullptr;
+  a.part_ml = num_splits > 1
+                  ? reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) + units * MLA_LATENT_DIM)
+                  : nullptr;
   a.o_latent = static_cast<uint16_t*>(o_latent);
   a.lse = lse;
   a.flags = flags;
@@ -196,8 +198,8 @@ int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_s
   if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
   const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
   mla::CombineArgs a;
-  a.part_acc = static_cast<const float*>(workspace);
-  a.part_ml = static_cast<const float*>(workspace) + units * MLA_LATENT_DIM;
+  a.part_o = static_cast<const uint16_t*>(workspace);
+  a.part_ml = reinterpret_cast<const float*>(static_cast<const uint16_t*>(workspace) + units * MLA_LATENT_DIM);
   a.B = B;
   a.S = num_splits;
   a.o_latent = static_cast<uint16_t*>(o_latent);
@@ -213,13 +215,37 @@ int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
   if (!aligned16(o_latent) || !aligned16(wkv_b) || !aligned16(out) || !stride8(out_sb) ||
       !stride8(out_sh))
     return MLA_ERR_ALIGNMENT;
-  mla::ValueUpArgs a;
+  mla::ValueUpArgs a = {};
   a.o_latent = static_cast<const uint16_t*>(o_latent);
   a.wkv_b = static_cast<const uint16_t*>(wkv_b);
   a.out = static_cast<uint16_t*>(out);
   a.out_sb = out_sb;
   a.out_sh = out_sh;
   a.B = B;
+  return hip_status(mla::launch_value_up(a, stream));
+}
+
+int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                         const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh, float* lse,
+                         uint32_t* status_dev, void* stream) {
+  if (B < 1 || B > 65536 || num_splits < 2 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
+  if (!workspace || !wkv_b || !out) return MLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace) || !aligned16(wkv_b) || !aligned16(out) || !stride8(out_sb) || !stride8(out_sh))
+    return MLA_ERR_ALIGNMENT;
+  if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  mla::ValueUpArgs a = {};
+  a.o_latent = nullptr;
+  a.wkv_b = static_cast<const uint16_t*>(wkv_b);
+  a.out = static_cast<uint16_t*>(out);
+  a.out_sb = out_sb;
+  a.out_sh = out_sh;
+  a.B = B;
+  a.part_o = static_cast<const uint16_t*>(workspace);
+  a.part_ml = reinterpret_cast<const float*>(static_cast<const uint16_t*>(workspace) + units * MLA_LATENT_DIM);
+  a.S = num_splits;
+  a.lse = lse;
+  a.status = status_dev;
   return hip_status(mla::launch_value_up(a, stream));
 }
 

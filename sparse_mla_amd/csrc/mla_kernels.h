@@ -40,8 +40,8 @@ struct DecodeArgs {
   int32_t S;                // splits
   float scale;              // softmax scale
   float scale_log2;         // softmax scale * log2(e)
-  float* part_acc;          // [S][B][128][512] when S > 1
-  float* part_ml;           // [S][B][128][2]   when S > 1
+  uint16_t* part_o;         // [S][B][128][512] bf16, normalised per split (S > 1)
+  float* part_ml;           // [S][B][128][2]   (max, sum) per split      (S > 1)
   uint16_t* o_latent;       // [B][128][512]    when S == 1
   float* lse;               // [B][128]         when S == 1 (may be NULL)
   uint32_t flags;
@@ -52,7 +52,7 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-  const float* part_acc;
+  const uint16_t* part_o;
   const float* part_ml;
   int32_t B, S;
   uint16_t* o_latent;
@@ -61,11 +61,17 @@ struct CombineArgs {
 };
 
 struct ValueUpArgs {
-  const uint16_t* o_latent;
+  const uint16_t* o_latent;  // [B][128][512]; NULL when the split partials are combined here
   const uint16_t* wkv_b;
   uint16_t* out;
   int64_t out_sb, out_sh;
   int32_t B;
+  // Fused combine (o_latent == NULL): partials of mla_sparse_decode.
+  const uint16_t* part_o;
+  const float* part_ml;
+  int32_t S;
+  float* lse;
+  uint32_t* status;
 };
 
 struct DequantArgs {
@@ -78,7 +84,7 @@ struct DequantArgs {
 int launch_absorb(const AbsorbArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, int head_groups, void* stream);
 int launch_combine(const CombineArgs& a, void* stream);
-int launch_value_up(const ValueUpArgs& a, void* stream);
+int launch_value_up(const ValueUpArgs& a, void* stream);  // fused combine when o_latent == NULL
 int launch_dequant(const DequantArgs& a, void* stream);
 int device_cu_count(int* cus);
 

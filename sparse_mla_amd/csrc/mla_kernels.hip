@@ -47,6 +47,12 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr uint32_t kMaskedOffset = 0x80000000u; // beyond every record range: loads 0
 
+// 16-byte position swizzle inside a 128-byte LDS segment, from key bits b0..b3:
+// (b2, b1, b0 ^ b1 ^ b3).
+__device__ __forceinline__ uint32_t seg_swz(uint32_t key) {
+  return ((key >> 2) & 1u) | (key & 2u) | (((key ^ (key >> 1) ^ (key >> 3)) & 1u) << 2);
+}
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource: 48-bit base, stride 0, num_records bytes, 32-bit data
@@ -110,45 +116,64 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 
 // ---------------------------------------------------------------------------
 // absorb: q_abs[b][h][c] = sum_d q_nope[b][h][d] W_UK,h[d][c]
-// Workgroup = (head, 128-column tile); wave w owns columns 32w .. 32w+31 and
-// loops over 32-row batch tiles.  W_UK is stored [d][c] (c contiguous) while
-// d is the reduction index, so the W tile is staged in LDS and read back with
-// transpose reads.  M = c (32), N = b (32), K = d (128).
+// Workgroup = (head, 64-column tile): 1024 workgroups.  W_UK is stored [d][c]
+// (c contiguous) while d is the reduction index, so the 128 x 64 tile is
+// moved into LDS by LDS-DMA (8 lanes per 128-byte row, chunk q of row d at
+// 16-byte position q ^ 2 (d % 4), which keeps the transpose reads
+// conflict-free) and read back as K-strided MFMA fragments.  Each wave takes
+// (32-column subtile, 32-row batch tile) pairs: M = c, N = b, K = d.  The
+// query operand of the first pair is loaded while the tile is in flight.
 // ---------------------------------------------------------------------------
-constexpr int kAbsRowStride = 160;  // LDS row stride in elements (128 + 32 pad)
-
 __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kNope * kAbsRowStride];
-  const int h = blockIdx.x >> 2, ctile = blockIdx.x & 3;
+  __shared__ __attribute__((aligned(1024))) char wt[kNope * 128];
+  const int h = blockIdx.x >> 3, ctile = blockIdx.x & 7;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint16_t* w = a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ctile * 128;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int id = i * 256 + tid, row = id >> 4, cc = id & 15;
-    *reinterpret_cast<uint4*>(wt + row * kAbsRowStride + cc * 8) =
-        *reinterpret_cast<const uint4*>(w + (size_t)row * kLatent + cc * 8);
-  }
-  __syncthreads();
-
-  const int i16 = lane & 15, gm = (lane >> 4) & 1, hh = lane >> 5;
+  const int hh = lane >> 5, i16 = lane & 15, gm = (lane >> 4) & 1;
   const char LDS_AS* wl = (const char LDS_AS*)wt;
-  bf16x8 af[8];
+  {
+    const i32x4 rw = buffer_rsrc(a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ctile * 64,
+                                 (uint32_t)((kNope - 1) * kLatent * 2 + 128));
+    const uint32_t lds0 = (uint32_t)(uintptr_t)wl;
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const int row0 = 16 * st + 8 * hh + (i16 >> 2);
-    const int col = wave * 32 + 16 * gm + 4 * (i16 & 3);
-    af[st] = tr_pair(wl + (row0 * kAbsRowStride + col) * 2, wl + ((row0 + 4) * kAbsRowStride + col) * 2);
+    for (int k = 0; k < 4; ++k) {
+      const int ins = wave * 4 + k;
+      const uint32_t d = (uint32_t)(8 * ins + (lane >> 3));
+      const uint32_t q = (uint32_t)(lane & 7) ^ (2u * (d & 3u));
+      dma16(rw, lds0 + (uint32_t)ins * 1024u, d * (uint32_t)(kLatent * 2) + q * 16u);
+    }
   }
-  for (int b0 = 0; b0 < a.B; b0 += 32) {
-    const int bb = b0 + (lane & 31);
+  const int nbt = (a.B + 31) / 32;
+  const int npairs = 2 * nbt;
+  bf16x8 qb[8];
+  auto load_q = [&](int bt) {
+    const int bb = bt * 32 + (lane & 31);
     const bool ok = bb < a.B;
     const uint16_t* q = a.q_nope + (int64_t)(ok ? bb : 0) * a.q_sb + (int64_t)h * a.q_sh + 8 * hh;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qb[st] = ok ? ld8(q + 16 * st) : zero8();
+  };
+  if (wave < npairs) load_q(wave >> 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int pi = wave; pi < npairs; pi += 4) {
+    const int ws = pi & 1, bt = pi >> 1;
+    if (pi != wave) load_q(bt);
     f32x16 acc = {};
 #pragma unroll
-    for (int st = 0; st < 8; ++st) acc = mfma32(af[st], ok ? ld8(q + 16 * st) : zero8(), acc);
-    if (ok) {
-      uint16_t* o = a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ctile * 128 + wave * 32 + 4 * hh;
+    for (int st = 0; st < 8; ++st) {
+      uint32_t off[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t d = (uint32_t)(16 * st + 8 * hh + 4 * r + (i16 >> 2));
+        const uint32_t q = (uint32_t)(4 * ws + 2 * gm + ((i16 & 3) >> 1));
+        off[r] = d * 128u + ((q ^ (2u * (d & 3u))) * 16u) + 8u * (uint32_t)(i16 & 1);
+      }
+      acc = mfma32(tr_pair(wl + off[0], wl + off[1]), qb[st], acc);
+    }
+    const int bb = bt * 32 + (lane & 31);
+    if (bb < a.B) {
+      uint16_t* o = a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ctile * 64 + ws * 32 + 4 * hh;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<uint2*>(o + 8 * q4) =
@@ -158,32 +183,104 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// value-up: out[b][h][d] = sum_c o_latent[b][h][c] W_UV,h[d][c]
-// One wave per (head, 32-row d tile): M = d, N = b, K = c (512).  Both
-// operands are contiguous along c, so they load straight from HBM; the W_UV
-// fragment (32 x 512) stays in registers across batch tiles.
+// value-up: out[b][h][d] = sum_c O~[b][h][c] W_UV,h[d][c]
+// Workgroup = (head, 32-row d tile): 512 workgroups; wave w reduces over
+// latent columns 128 w .. 128 w + 127 and the four partial 32 x 32 tiles are
+// summed through LDS.  M = d, N = b, K = c; both operands are contiguous
+// along c and load straight from memory.  FUSED: the O~ operand is merged
+// here from the split partials of the decode ("Softmax" page, normalisation
+// over all selected keys): O~ = sum_s g_s O~_s with g_s = 2^(m_s - M) l_s / L,
+// L = sum_s 2^(m_s - M) l_s, and lse = ln 2 (M + log2 L).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void value_up_kernel(const ValueUpArgs a) {
+template <bool FUSED>
+__global__ __launch_bounds__(256) void value_up_kernel(const ValueUpArgs a) {
+  __shared__ float red[3][4][16][64];
   const int h = blockIdx.x >> 2, dt = blockIdx.x & 3;
-  const int lane = threadIdx.x, hh = lane >> 5;
-  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + dt * 32 + (lane & 31)) * kLatent + 8 * hh;
-  bf16x8 wf[32];
+  const int lane = threadIdx.x & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = wave * 128 + 8 * hh;
+  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + dt * 32 + (lane & 31)) * kLatent + c0;
+  bf16x8 wf[8];
 #pragma unroll
-  for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
-  for (int b0 = 0; b0 < a.B; b0 += 32) {
-    const int bb = b0 + (lane & 31);
-    const bool ok = bb < a.B;
-    const uint16_t* o = a.o_latent + ((int64_t)(ok ? bb : 0) * kHeads + h) * kLatent + 8 * hh;
-    f32x16 acc = {};
+  for (int st = 0; st < 8; ++st) wf[st] = ld8(w + 16 * st);
+  const int nbt = (a.B + 31) / 32;
+  const int64_t sstride = (int64_t)a.B * kHeads;
+  for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
+    f32x16 acc[4];
 #pragma unroll
-    for (int st = 0; st < 32; ++st) acc = mfma32(wf[st], ok ? ld8(o + 16 * st) : zero8(), acc);
-    if (ok) {
-      uint16_t* out = a.out + (int64_t)bb * a.out_sb + (int64_t)h * a.out_sh + dt * 32 + 4 * hh;
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = f32x16{};
+      const int bt = bt0 + t;
+      if (bt >= nbt) continue;
+      const int bb = bt * 32 + (lane & 31);
+      const bool ok = bb < a.B;
+      const int64_t bh = (int64_t)(ok ? bb : 0) * kHeads + h;
+      if constexpr (FUSED) {
+        float M = -INFINITY;
+        for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[(s * sstride + bh) * 2]);
+        float L = 0.f;
+        for (int s = 0; s < a.S; ++s) {
+          const float ms = a.part_ml[(s * sstride + bh) * 2];
+          L += (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * a.part_ml[(s * sstride + bh) * 2 + 1];
+        }
+        const float invL = 1.0f / L;
+        float comb[8][8];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<uint2*>(out + 8 * q4) =
-            pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) comb[st][e] = 0.f;
+        for (int s = 0; s < a.S; ++s) {
+          const float ms = a.part_ml[(s * sstride + bh) * 2];
+          const float g = (ms == -INFINITY) ? 0.f
+                              : __builtin_amdgcn_exp2f(ms - M) * a.part_ml[(s * sstride + bh) * 2 + 1] * invL;
+          const uint16_t* ps = a.part_o + (s * sstride + bh) * kLatent + c0;
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            const bf16x8 v = ld8(ps + 16 * st);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) comb[st][e] += g * (float)v[e];
+          }
+        }
+        const float empty = L > 0.f ? 0.f : __builtin_nanf("");  // all -inf row: NaN, as in mla_combine
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          bf16x8 bo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bo[e] = (__bf16)(comb[st][e] + empty);
+          acc[t] = mfma32(wf[st], ok ? bo : zero8(), acc[t]);
+        }
+        if (wave == 0 && dt == 0 && hh == 0 && ok) {
+          if (a.lse != nullptr) a.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+          if (a.status != nullptr && h == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
+        }
+      } else {
+        const uint16_t* o = a.o_latent + bh * kLatent + c0;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) acc[t] = mfma32(wf[st], ok ? ld8(o + 16 * st) : zero8(), acc[t]);
+      }
     }
+    if (wave > 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[wave - 1][t][v][lane] = acc[t][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int bb = (bt0 + t) * 32 + (lane & 31);
+        if (bt0 + t >= nbt || bb >= a.B) continue;
+        float r[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) r[v] = acc[t][v] + red[0][t][v][lane] + red[1][t][v][lane] + red[2][t][v][lane];
+        uint16_t* out = a.out + (int64_t)bb * a.out_sb + (int64_t)h * a.out_sh + dt * 32 + 4 * hh;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<uint2*>(out + 8 * q4) = pack4(r[4 * q4], r[4 * q4 + 1], r[4 * q4 + 2], r[4 * q4 + 3]);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -198,10 +295,13 @@ __global__ __launch_bounds__(64) void value_up_kernel(const ValueUpArgs a) {
 // in flight.  Masked slots get an offset past the record range, so their
 // rows arrive as zeros.
 //
-// LDS block layout: 16-byte slot (chunk c, key k) at c * NKEY + (k ^ sw(c)),
-// chunk c = 8 consecutive features of the 576-feature row [latent | rotary],
-// sw(c) = 8 ((c >> 1) & 1): rows are read contiguously by the score MFMA and
-// the transpose reads of the mix MFMA spread over all banks.
+// LDS block layout: a row [latent 512 | rotary 64] is 9 lines of 128 bytes
+// (8 chunks of 8 features each).  Line m of key k is the 128-byte segment
+// (m * NKEY + k) * 128, and chunk q of that line sits at 16-byte position
+// q ^ sw(k).  One gather instruction moves 8 segments (8 keys, one line
+// each): 8 adjacent lanes read one whole 128-byte line of one row.  sw() is
+// chosen so that the score reads (32 keys, one chunk) and the transpose
+// reads (8 keys x 4 chunks) hit distinct banks for 32- and 64-bank LDS.
 //
 // Per wave and block of 32 keys:
 //   scores  S^T[key][head] = sum_f row[key][f] Q~[head][f]: A = rows (LDS,
@@ -302,26 +402,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)b * a.pe_sb, (uint32_t)Lb * pe_rb);
   const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
 
-  // Gather block p into buffer p % NBUF.  A lane's slot in instruction g is
-  // g * 64 + lane; its key is (lane % NKEY) or that ^ 8, per sw(chunk).
+  // Gather block p into buffer p % NBUF.  Wave w moves key groups
+  // (8 keys each) KL*w .. KL*w+KL-1, all 9 lines; lane l takes key
+  // 8 * group + l / 8 and 16-byte position l % 8 of each line.
   auto issue = [&](int p) {
-    const int kA = lane & (NKEY - 1);
-    const int rA = row_of(p * NKEY + kA), rB = row_of(p * NKEY + (kA ^ 8));
-    const uint32_t okA = rA >= 0 ? (uint32_t)rA * kv_rb : kMaskedOffset;
-    const uint32_t okB = rB >= 0 ? (uint32_t)rB * kv_rb : kMaskedOffset;
-    const uint32_t opA = rA >= 0 ? (uint32_t)rA * pe_rb : kMaskedOffset;
-    const uint32_t opB = rB >= 0 ? (uint32_t)rB * pe_rb : kMaskedOffset;
-    const uint32_t dst = lds0 + (uint32_t)((p % NBUF) * BUF);
+    const uint32_t dst0 = lds0 + (uint32_t)((p % NBUF) * BUF);
 #pragma unroll
-    for (int i = 0; i < GPW; ++i) {
-      const int g = wave * GPW + i;
-      const int cb = (g * 64) / NKEY;            // chunk of lane 0 (uniform)
-      const int c = (g * 64 + lane) / NKEY;      // this lane's chunk
-      const bool useB = (cb >> 1) & 1;
-      const bool isPe = cb >= 64;
-      const uint32_t off = isPe ? (useB ? opB : opA) + (uint32_t)(c - 64) * 16
-                                : (useB ? okB : okA) + (uint32_t)c * 16;
-      dma16(isPe ? rpe : rkv, dst + (uint32_t)g * 1024, off);
+    for (int kg = 0; kg < KL; ++kg) {
+      const int key = 8 * (KL * wave + kg) + (lane >> 3);
+      const int row = row_of(p * NKEY + key);
+      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz((uint32_t)key)) * 16u;
+      const uint32_t okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
+      const uint32_t ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
+      const uint32_t dst = dst0 + (uint32_t)(8 * (KL * wave + kg)) * 128u;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) dma16(rkv, dst + (uint32_t)(m * NKEY * 128), okv + (uint32_t)(m * 128));
+      dma16(rpe, dst + (uint32_t)(8 * NKEY * 128), ope);
     }
   };
 
@@ -330,12 +426,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   for (int ct = 0; ct < 16; ++ct) acc[ct] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Per-lane LDS offsets.
-  const uint32_t qk_e = (uint32_t)((hh * NKEY + kl * 32 + (lane & 31)) * 16);
-  const uint32_t qk_o = (uint32_t)((hh * NKEY + kl * 32 + ((lane & 31) ^ 8)) * 16);
+  // Per-lane LDS offsets.  Score reads: key kl*32 + lane%32, chunk
+  // 2 st + hh (line st / 4, chunk-in-line 2 (st % 4) + hh).
+  uint32_t qk_base[4];
+  {
+    const uint32_t key = (uint32_t)(kl * 32 + (lane & 31));
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      qk_base[s4] = key * 128u + (((uint32_t)(2 * s4 + hh)) ^ seg_swz(key)) * 16u;
+  }
+  // Transpose reads: source lane i of group g reads key
+  // kl*32 + 16 ks + 8 r + 4 hh + i/4, columns 32 ct + 16 gm + 4 (i % 4):
+  // chunk-in-line 4 (ct % 2) + 2 gm + (i % 4) / 2, byte 8 (i % 2).
   const int i16 = lane & 15, gm = (lane >> 4) & 1;
-  const uint32_t pc_base = (uint32_t)(((2 * gm + ((i16 & 3) >> 1)) * NKEY + kl * 32 + 4 * hh + (i16 >> 2)) * 16 + 8 * (i16 & 1));
-  const uint32_t pc_r0 = pc_base + gm * 128, pc_r1 = pc_base + (gm ^ 1) * 128;
+  uint32_t pc_base[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1) {
+      const uint32_t key = (uint32_t)(kl * 32 + 8 * r + 4 * hh + (i16 >> 2));
+      const uint32_t q = (uint32_t)(4 * c1 + 2 * gm + ((i16 & 3) >> 1));
+      pc_base[r][c1] = key * 128u + ((q ^ seg_swz(key)) * 16u) + 8u * (uint32_t)(i16 & 1);
+    }
 
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
@@ -364,7 +476,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       constexpr int QK_AHEAD = 3;
       bf16x8 ring[QK_AHEAD + 1];
       auto qk_ld = [&](int st) {
-        const uint32_t off = ((st & 1) ? qk_o : qk_e) + (uint32_t)(st * 2 * NKEY * 16);
+        const uint32_t off = qk_base[st & 3] + (uint32_t)((st >> 2) * NKEY * 128);
         return *(const bf16x8 LDS_AS*)(buf + off);
       };
 #pragma unroll
@@ -436,8 +548,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       constexpr int PC_AHEAD = 3;
       bf16x8 ring[PC_AHEAD + 1];
       auto pc_ld = [&](int i) {  // i = 2 ct + ks
-        const uint32_t o = (uint32_t)((i >> 1) * 4 * NKEY * 16 + (i & 1) * 256);
-        return tr_pair(buf + pc_r0 + o, buf + pc_r1 + o);
+        const int ct = i >> 1, ks = i & 1;
+        const uint32_t o = (uint32_t)((ct >> 1) * NKEY * 128 + ks * 16 * 128);
+        return tr_pair(buf + pc_base[0][ct & 1] + o, buf + pc_base[1][ct & 1] + o);
       };
 #pragma unroll
       for (int i = 0; i < PC_AHEAD; ++i) ring[i] = pc_ld(i);
@@ -494,13 +607,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       a.lse[(int64_t)b * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
     if (validate && hs == 0 && lane == 0 && !(l_run > 0.f)) atomicOr(a.status, 4u);
   } else {
-    float* pa = a.part_acc + (((int64_t)s * a.B + b) * kHeads + head) * kLatent + 4 * hh;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;  // an empty split contributes nothing
+    uint16_t* po = a.part_o + (((int64_t)s * a.B + b) * kHeads + head) * kLatent + 4 * hh;
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4*>(pa + 32 * ct + 8 * q4) =
-            f32x4{acc[ct][4 * q4], acc[ct][4 * q4 + 1], acc[ct][4 * q4 + 2], acc[ct][4 * q4 + 3]};
+        *reinterpret_cast<uint2*>(po + 32 * ct + 8 * q4) =
+            pack4(acc[ct][4 * q4] * inv, acc[ct][4 * q4 + 1] * inv, acc[ct][4 * q4 + 2] * inv,
+                  acc[ct][4 * q4 + 3] * inv);
     if (hh == 0) {
       float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + head) * 2;
       pml[0] = m_run;
@@ -510,7 +625,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: O~ = sum_s w_s acc_s / sum_s w_s l_s, w_s = 2^(m_s - max m)
+// combine: O~ = sum_s g_s O~_s, g_s = 2^(m_s - M) l_s / L, L = sum_s 2^(m_s - M) l_s
 // Workgroup = (sequence, 2 heads); each thread owns 4 latent columns.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
@@ -525,9 +640,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.S; ++s) {
     const float ms = a.part_ml[(s * stride_s + bh) * 2];
-    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L += w * a.part_ml[(s * stride_s + bh) * 2 + 1];
-    acc += w * *reinterpret_cast<const f32x4*>(a.part_acc + (s * stride_s + bh) * kLatent + col);
+    const float wl = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * a.part_ml[(s * stride_s + bh) * 2 + 1];
+    L += wl;
+    const uint2 v = *reinterpret_cast<const uint2*>(a.part_o + (s * stride_s + bh) * kLatent + col);
+    acc[0] += wl * __uint_as_float(v.x << 16);
+    acc[1] += wl * __uint_as_float(v.x & 0xffff0000u);
+    acc[2] += wl * __uint_as_float(v.y << 16);
+    acc[3] += wl * __uint_as_float(v.y & 0xffff0000u);
   }
   const float inv = 1.0f / L;
   *reinterpret_cast<uint2*>(a.o_latent + bh * kLatent + col) =
@@ -592,7 +711,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 }  // namespace
 
 int launch_absorb(const AbsorbArgs& a, void* stream) {
-  hipLaunchKernelGGL(absorb_kernel, dim3(kHeads * 4), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(absorb_kernel, dim3(kHeads * 8), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
@@ -617,7 +736,10 @@ int launch_combine(const CombineArgs& a, void* stream) {
 }
 
 int launch_value_up(const ValueUpArgs& a, void* stream) {
-  hipLaunchKernelGGL(value_up_kernel, dim3(kHeads * 4), dim3(64), 0, (hipStream_t)stream, a);
+  if (a.o_latent == nullptr)
+    hipLaunchKernelGGL(value_up_kernel<true>, dim3(kHeads * 4), dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(value_up_kernel<false>, dim3(kHeads * 4), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

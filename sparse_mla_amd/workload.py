@@ -165,9 +165,10 @@ def fp8_weights(rows: int, cols: int, seed: int, device="cpu"):
 
 def make(name_or_spec, device="cpu", B: Optional[int] = None, L: Optional[int] = None,
          k: Optional[int] = None, variant: int = 0, lens: Optional[torch.Tensor] = None,
-         cache_device=None) -> Workload:
+         cache_device=None, cache: Optional[torch.Tensor] = None) -> Workload:
     """Draw one workload.  B, L and k override the recipe (for small cases);
-    ``cache_device`` lets the large cache be drawn on the GPU."""
+    ``cache_device`` lets the large cache be drawn on the GPU; ``cache`` reuses
+    an existing cache tensor instead of drawing one."""
     spec = SPECS[name_or_spec] if isinstance(name_or_spec, str) else name_or_spec
     B = spec.B if B is None else B
     L = spec.L if L is None else L
@@ -180,7 +181,8 @@ def make(name_or_spec, device="cpu", B: Optional[int] = None, L: Optional[int] =
     max_len = int(lens.max())
     q_nope = _normal_bf16((B, 1, H, DN), _gen(device, seed + 0), device)
     q_pe = _normal_bf16((B, 1, H, DR), _gen(device, seed + 1), device)
-    cache = _normal_bf16((B, L, DQK), _gen(cdev, seed + 2), cdev)
+    if cache is None:
+        cache = _normal_bf16((B, L, DQK), _gen(cdev, seed + 2), cdev)
     if spec.fp8:
         codes, sc = fp8_weights(H * (DN + DV), DC, seed, device)
         wkv_b = None

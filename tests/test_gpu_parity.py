@@ -49,7 +49,7 @@ def test_value_up(mla):
     assert rel_err(f64(out)[:, 0], oracle.value_up(o_lat, w.wkv_b)) <= 4e-3
 
 
-def _run_decode(mla, g, S, HG, layout="packed", flags=0, bitmap=None, scores=None, status=None):
+def _run_decode(mla, g, S, HG, layout="packed", flags=0, bitmap=None, scores=None, status=None, fused=False):
     B = g.B
     k_max = g.k_max
     bufs = mla.DecodeBuffers.allocate(B, k_max, g.indices is None, num_splits=S, head_groups=HG)
@@ -58,7 +58,7 @@ def _run_decode(mla, g, S, HG, layout="packed", flags=0, bitmap=None, scores=Non
     else:  # two buffers, as in the pages' code
         kv, pe = g.kv.contiguous(), g.pe.contiguous()
     out = mla.decode_step(bufs, g.q_nope, g.q_pe, kv, pe, g.wkv_b, g.seq_lens, g.max_len, g.indices,
-                          g.scale, flags=flags, bitmap=bitmap, scores=scores, status=status)
+                          g.scale, flags=flags, bitmap=bitmap, scores=scores, status=status, fused=fused)
     torch.cuda.synchronize()
     return bufs, out
 
@@ -89,6 +89,11 @@ def test_decode_small(mla, case):
     assert rel_err(f64(bufs.o_latent), ref["o_lat"]) <= REL_TOL
     assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
     assert rowsum_dev(ref["scores"], f64(bufs.lse)) <= ROWSUM_TOL
+    if S > 1:  # combine fused into the value-up launch
+        bufs.lse.fill_(float("nan"))
+        bufs2, out2 = _run_decode(mla, g, S, HG, layout, fused=True)
+        assert rel_err(f64(out2)[:, 0], ref["out"]) <= REL_TOL
+        assert rowsum_dev(ref["scores"], f64(bufs2.lse)) <= ROWSUM_TOL
 
 
 def test_decode_validate_bitmap_and_scores(mla):
@@ -121,8 +126,8 @@ def test_decode_validate_bitmap_and_scores(mla):
     assert rowsum_dev(sc, f64(bufs.lse)) <= ROWSUM_TOL
 
 
-@pytest.mark.parametrize("S,HG", [(1, 1), (2, 2)])
-def test_decode_validate_errors(mla, S, HG):
+@pytest.mark.parametrize("S,HG,fused", [(1, 1, False), (2, 2, False), (2, 2, True)])
+def test_decode_validate_errors(mla, S, HG, fused):
     """Out-of-range and repeated indices and an empty row set the status
     bits; the empty sequence yields NaN and the others stay finite."""
     w = workload.make("sparse_b32_l4096_k2048", B=3, L=200, k=64)
@@ -132,7 +137,8 @@ def test_decode_validate_errors(mla, S, HG):
     g = to_gpu(w)
     bitmap = torch.zeros((w.B, 8), dtype=torch.int32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    bufs, out = _run_decode(mla, g, S, HG, flags=mla.MLA_FLAG_VALIDATE, bitmap=bitmap, status=status)
+    bufs, out = _run_decode(mla, g, S, HG, flags=mla.MLA_FLAG_VALIDATE, bitmap=bitmap, status=status,
+                            fused=fused)
     st = int(status.item())
     assert st == (mla.MLA_DEV_INDEX_OUT_OF_RANGE | mla.MLA_DEV_DUPLICATE_INDEX | mla.MLA_DEV_EMPTY_SELECTION)
     o = f64(out)
