@@ -116,172 +116,209 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 
 // ---------------------------------------------------------------------------
 // absorb: q_abs[b][h][c] = sum_d q_nope[b][h][d] W_UK,h[d][c]
-// Workgroup = (head, 64-column tile): 1024 workgroups.  W_UK is stored [d][c]
-// (c contiguous) while d is the reduction index, so the 128 x 64 tile is
-// moved into LDS by LDS-DMA (8 lanes per 128-byte row, chunk q of row d at
-// 16-byte position q ^ 2 (d % 4), which keeps the transpose reads
-// conflict-free) and read back as K-strided MFMA fragments.  Each wave takes
-// (32-column subtile, 32-row batch tile) pairs: M = c, N = b, K = d.  The
-// query operand of the first pair is loaded while the tile is in flight.
+// Workgroup = (head, 256-column half): 256 workgroups, each streaming its
+// 64 KB slab of W_UK once and looping over 32-row batch tiles.  W_UK is
+// stored [d][c] (c contiguous)
+// while d is the reduction index, so the 128 x 256 slab (64 KB) is moved into
+// LDS by LDS-DMA -- 8 lanes per 128-byte line, line m of row d at segment
+// (m * 128 + d), chunk q at 16-byte position q ^ 2 (d % 4), which keeps the
+// transpose reads conflict-free -- and read back as K-strided MFMA fragments.
+// Wave w owns columns 64 w .. 64 w + 63 of the half (two 32-column tiles):
+// M = c, N = b, K = d.  The first query tiles load while the slab is in flight.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
-  __shared__ __attribute__((aligned(1024))) char wt[kNope * 128];
-  const int h = blockIdx.x >> 3, ctile = blockIdx.x & 7;
+  __shared__ __attribute__((aligned(1024))) char wt[4 * kNope * 128];
+  const int h = blockIdx.x & (kHeads - 1);
+  const int ch = blockIdx.x >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, i16 = lane & 15, gm = (lane >> 4) & 1;
   const char LDS_AS* wl = (const char LDS_AS*)wt;
   {
-    const i32x4 rw = buffer_rsrc(a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ctile * 64,
-                                 (uint32_t)((kNope - 1) * kLatent * 2 + 128));
+    const i32x4 rw = buffer_rsrc(a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ch * 256,
+                                 (uint32_t)((kNope - 1) * kLatent * 2 + 512));
     const uint32_t lds0 = (uint32_t)(uintptr_t)wl;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int ins = wave * 4 + k;
-      const uint32_t d = (uint32_t)(8 * ins + (lane >> 3));
+    for (int k = 0; k < 16; ++k) {
+      const int ins = wave * 16 + k;                   // line ins / 16, rows 8 (ins % 16) + 0..7
+      const uint32_t d = (uint32_t)(((ins & 15) << 3) + (lane >> 3));
       const uint32_t q = (uint32_t)(lane & 7) ^ (2u * (d & 3u));
-      dma16(rw, lds0 + (uint32_t)ins * 1024u, d * (uint32_t)(kLatent * 2) + q * 16u);
+      dma16(rw, lds0 + (uint32_t)ins * 1024u, d * (uint32_t)(kLatent * 2) + (uint32_t)(ins >> 4) * 128u + q * 16u);
     }
   }
+  // A operand (the slab, as K-strided fragments) is the same for every batch
+  // tile: read it once.  Query tiles are loaded four at a time.
   const int nbt = (a.B + 31) / 32;
-  const int npairs = 2 * nbt;
-  bf16x8 qb[8];
-  auto load_q = [&](int bt) {
-    const int bb = bt * 32 + (lane & 31);
-    const bool ok = bb < a.B;
-    const uint16_t* q = a.q_nope + (int64_t)(ok ? bb : 0) * a.q_sb + (int64_t)h * a.q_sh + 8 * hh;
+  bf16x8 qb[4][8];
+  auto load_q = [&](int bt0) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qb[st] = ok ? ld8(q + 16 * st) : zero8();
+    for (int u = 0; u < 4; ++u) {
+      // Rows past B load row B-1: they only feed output columns that are
+      // never stored, and unconditional loads keep all of them in flight.
+      const int bb = min((bt0 + u) * 32 + (lane & 31), a.B - 1);
+      const uint16_t* q = a.q_nope + (int64_t)bb * a.q_sb + (int64_t)h * a.q_sh + 8 * hh;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) qb[u][st] = ld8(q + 16 * st);
+    }
   };
-  if (wave < npairs) load_q(wave >> 1);
+  load_q(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int pi = wave; pi < npairs; pi += 4) {
-    const int ws = pi & 1, bt = pi >> 1;
-    if (pi != wave) load_q(bt);
-    f32x16 acc = {};
+  bf16x8 af[2][8];
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       uint32_t off[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const uint32_t d = (uint32_t)(16 * st + 8 * hh + 4 * r + (i16 >> 2));
-        const uint32_t q = (uint32_t)(4 * ws + 2 * gm + ((i16 & 3) >> 1));
-        off[r] = d * 128u + ((q ^ (2u * (d & 3u))) * 16u) + 8u * (uint32_t)(i16 & 1);
+        const uint32_t q = (uint32_t)(4 * t + 2 * gm + ((i16 & 3) >> 1));
+        off[r] = ((uint32_t)wave * kNope + d) * 128u + ((q ^ (2u * (d & 3u))) * 16u) + 8u * (uint32_t)(i16 & 1);
       }
-      acc = mfma32(tr_pair(wl + off[0], wl + off[1]), qb[st], acc);
+      af[t][st] = tr_pair(wl + off[0], wl + off[1]);
     }
-    const int bb = bt * 32 + (lane & 31);
-    if (bb < a.B) {
-      uint16_t* o = a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ctile * 64 + ws * 32 + 4 * hh;
+  for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
+    if (bt0 > 0) load_q(bt0);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<uint2*>(o + 8 * q4) =
-            pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    for (int u = 0; u < 4; ++u) {
+      const int bb = (bt0 + u) * 32 + (lane & 31);
+      if (bt0 + u >= nbt) break;
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma32(af[t][st], qb[u][st], acc[t]);
+      if (bb < a.B) {
+        uint16_t* o = a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + wave * 64 + 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<uint2*>(o + 32 * t + 8 * q4) =
+                pack4(acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // value-up: out[b][h][d] = sum_c O~[b][h][c] W_UV,h[d][c]
-// Workgroup = (head, 32-row d tile): 512 workgroups; wave w reduces over
-// latent columns 128 w .. 128 w + 127 and the four partial 32 x 32 tiles are
-// summed through LDS.  M = d, N = b, K = c; both operands are contiguous
-// along c and load straight from memory.  FUSED: the O~ operand is merged
-// here from the split partials of the decode ("Softmax" page, normalisation
-// over all selected keys): O~ = sum_s g_s O~_s with g_s = 2^(m_s - M) l_s / L,
-// L = sum_s 2^(m_s - M) l_s, and lse = ln 2 (M + log2 L).
+// Workgroup = head: 128 workgroups, each reading its 128 KB of W_UV once
+// (wave w keeps value rows 32 w .. 32 w + 31 in registers) and looping over
+// 32-row batch tiles.  Each O~ tile [32][512] is assembled in LDS (rows
+// padded to 1040 bytes, two buffers alternating), then wave w computes
+// value rows 32 w .. 32 w + 31: M = d (W_UV rows, contiguous along c, loaded
+// straight into registers while the tile is assembled), N = b (from LDS),
+// K = c.  FUSED: the tile is merged from the split partials of the decode
+// ("Softmax" page, normalisation over all selected keys):
+//   O~ = sum_s g_s O~_s, g_s = 2^(m_s - M) l_s / L, L = sum_s 2^(m_s - M) l_s,
+//   lse = ln 2 (M + log2 L)
 // ---------------------------------------------------------------------------
+constexpr int kOtRow = 1040;  // bytes per O~ row in LDS (512 bf16 + 16 pad)
+
 template <bool FUSED>
 __global__ __launch_bounds__(256) void value_up_kernel(const ValueUpArgs a) {
-  __shared__ float red[3][4][16][64];
-  const int h = blockIdx.x >> 2, dt = blockIdx.x & 3;
-  const int lane = threadIdx.x & 63, hh = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c0 = wave * 128 + 8 * hh;
-  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + dt * 32 + (lane & 31)) * kLatent + c0;
-  bf16x8 wf[8];
+  __shared__ __attribute__((aligned(16))) char ot[2][32 * kOtRow];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
+  bf16x8 wf[32];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) wf[st] = ld8(w + 16 * st);
+  for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
+
   const int nbt = (a.B + 31) / 32;
-  const int64_t sstride = (int64_t)a.B * kHeads;
-  for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
-    f32x16 acc[4];
+  for (int bt = 0; bt < nbt; ++bt) {
+  char* tile = ot[bt & 1];
+  // O~ tile: wave w fills rows 8 w .. 8 w + 7; lane l owns columns
+  // 8 l .. 8 l + 7 of each row (one coalesced 1 KB line per load).  All loads
+  // of a pass are issued before any of them is used; rows past B read row
+  // B-1 and are written as zeros.
+  int64_t bh[8];
+  bool okr[8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[t] = f32x16{};
-      const int bt = bt0 + t;
-      if (bt >= nbt) continue;
-      const int bb = bt * 32 + (lane & 31);
-      const bool ok = bb < a.B;
-      const int64_t bh = (int64_t)(ok ? bb : 0) * kHeads + h;
-      if constexpr (FUSED) {
-        float M = -INFINITY;
-        for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[(s * sstride + bh) * 2]);
-        float L = 0.f;
-        for (int s = 0; s < a.S; ++s) {
-          const float ms = a.part_ml[(s * sstride + bh) * 2];
-          L += (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * a.part_ml[(s * sstride + bh) * 2 + 1];
-        }
-        const float invL = 1.0f / L;
-        float comb[8][8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) comb[st][e] = 0.f;
-        for (int s = 0; s < a.S; ++s) {
-          const float ms = a.part_ml[(s * sstride + bh) * 2];
-          const float g = (ms == -INFINITY) ? 0.f
-                              : __builtin_amdgcn_exp2f(ms - M) * a.part_ml[(s * sstride + bh) * 2 + 1] * invL;
-          const uint16_t* ps = a.part_o + (s * sstride + bh) * kLatent + c0;
-#pragma unroll
-          for (int st = 0; st < 8; ++st) {
-            const bf16x8 v = ld8(ps + 16 * st);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) comb[st][e] += g * (float)v[e];
-          }
-        }
-        const float empty = L > 0.f ? 0.f : __builtin_nanf("");  // all -inf row: NaN, as in mla_combine
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          bf16x8 bo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bo[e] = (__bf16)(comb[st][e] + empty);
-          acc[t] = mfma32(wf[st], ok ? bo : zero8(), acc[t]);
-        }
-        if (wave == 0 && dt == 0 && hh == 0 && ok) {
-          if (a.lse != nullptr) a.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-          if (a.status != nullptr && h == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
-        }
-      } else {
-        const uint16_t* o = a.o_latent + bh * kLatent + c0;
-#pragma unroll
-        for (int st = 0; st < 8; ++st) acc[t] = mfma32(wf[st], ok ? ld8(o + 16 * st) : zero8(), acc[t]);
-      }
-    }
-    if (wave > 0) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) red[wave - 1][t][v][lane] = acc[t][v];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int bb = (bt0 + t) * 32 + (lane & 31);
-        if (bt0 + t >= nbt || bb >= a.B) continue;
-        float r[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) r[v] = acc[t][v] + red[0][t][v][lane] + red[1][t][v][lane] + red[2][t][v][lane];
-        uint16_t* out = a.out + (int64_t)bb * a.out_sb + (int64_t)h * a.out_sh + dt * 32 + 4 * hh;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<uint2*>(out + 8 * q4) = pack4(r[4 * q4], r[4 * q4 + 1], r[4 * q4 + 2], r[4 * q4 + 3]);
-      }
-    }
-    __syncthreads();
+  for (int j = 0; j < 8; ++j) {
+    const int bb = bt * 32 + 8 * wave + j;
+    okr[j] = bb < a.B;
+    bh[j] = (int64_t)min(bb, a.B - 1) * kHeads + h;
   }
+  float v[8][8];
+  if constexpr (FUSED) {
+    // Lane s holds split s's (max, sum); the merge weights come from two wave
+    // reductions per row and are broadcast to all lanes.
+    const int64_t sstride = (int64_t)a.B * kHeads;
+    const int ls = min(lane, a.S - 1);
+    float2 ml[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ml[j] = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)ls * sstride + bh[j]) * 2);
+    float g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float m = lane < a.S ? ml[j].x : -INFINITY;
+      float M = m;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+      const float e = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[j].y;
+      float L = e;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+      g[j] = e / L;
+      const float empty = L > 0.f ? 0.f : __builtin_nanf("");  // all -inf row: NaN, as in mla_combine
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[j][k] = empty;
+      if (lane == 0 && okr[j]) {
+        if (a.lse != nullptr) a.lse[bh[j]] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        if (a.status != nullptr && h == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
+      }
+    }
+    for (int s0 = 0; s0 < a.S; s0 += 2) {
+      bf16x8 x[8][2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          x[j][u] = ld8(a.part_o + ((int64_t)min(s0 + u, a.S - 1) * sstride + bh[j]) * kLatent + 8 * lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float gs = (s0 + u < a.S) ? __shfl(g[j], s0 + u) : 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[j][u][k];
+        }
+    }
+  } else {
+    bf16x8 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = ld8(a.o_latent + bh[j] * kLatent + 8 * lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[j][k] = (float)x[j][k];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bf16x8 y;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = okr[j] ? (__bf16)v[j][k] : (__bf16)0.f;
+    *reinterpret_cast<bf16x8*>(tile + (8 * wave + j) * kOtRow + 16 * lane) = y;
+  }
+  __syncthreads();
+
+  f32x16 acc = {};
+  const char LDS_AS* ol = (const char LDS_AS*)tile + (lane & 31) * kOtRow + 16 * hh;
+#pragma unroll
+  for (int st = 0; st < 32; ++st) acc = mfma32(wf[st], *(const bf16x8 LDS_AS*)(ol + 32 * st), acc);
+  const int bb = bt * 32 + (lane & 31);
+  if (bb < a.B) {
+    uint16_t* out = a.out + (int64_t)bb * a.out_sb + (int64_t)h * a.out_sh + 32 * wave + 4 * hh;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<uint2*>(out + 8 * q4) = pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+  }
+  }  // batch tiles (two tile buffers: one barrier per tile suffices)
 }
 
 // ---------------------------------------------------------------------------
@@ -351,25 +388,50 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B layout.
   bf16x8 qf[36];
-  {
+  auto load_query = [&]() {
     const uint16_t* qa = a.q_abs + ((int64_t)b * kHeads + head) * kLatent + 8 * hh;
 #pragma unroll
     for (int st = 0; st < 32; ++st) qf[st] = ld8(qa + 16 * st);
     const uint16_t* qp = a.q_pe + (int64_t)b * a.q_pe_sb + (int64_t)head * a.q_pe_sh + 8 * hh;
 #pragma unroll
     for (int st = 0; st < 4; ++st) qf[32 + st] = ld8(qp + 16 * st);
-  }
+  };
 
   // Stage this split's index slots as cache rows (-1 = masked).  The same
   // predicate decides validity, the attended bitmap and the device checks.
+  // Thread t owns slots 4 t .. 4 t + 3 of each 1024-slot pass; all of its
+  // loads are issued before any is used.
   if constexpr (!dense) {
-    for (int i = tid; i < nblk * NKEY; i += 256) {
-      int row = -1;
-      if (i < nslot) {
-        const int t = a.indices[(int64_t)b * a.k_max + s0 + i];
-        const bool ok = t >= 0 && t < Lb;
-        row = ok ? t : -1;
-        if (validate) {
+    constexpr int kPass = 4 * 256;
+    int4 raw[kIdxCap / kPass];
+#pragma unroll
+    for (int ps = 0; ps < kIdxCap / kPass; ++ps) {
+      const int i0 = ps * kPass + 4 * tid;
+      const int64_t base = (int64_t)b * a.k_max + s0 + i0;
+      if (i0 + 3 < nslot && (base & 3) == 0) {
+        raw[ps] = *reinterpret_cast<const int4*>(a.indices + base);
+      } else {
+        raw[ps].x = i0 + 0 < nslot ? a.indices[base + 0] : -1;
+        raw[ps].y = i0 + 1 < nslot ? a.indices[base + 1] : -1;
+        raw[ps].z = i0 + 2 < nslot ? a.indices[base + 2] : -1;
+        raw[ps].w = i0 + 3 < nslot ? a.indices[base + 3] : -1;
+      }
+    }
+    // The query operand loads go out after the index loads and stay in
+    // flight: vmcnt retires in order, so waiting for the indices leaves the
+    // 36 query loads outstanding, and the first block's wait covers them.
+    load_query();
+    asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+#pragma unroll
+    for (int ps = 0; ps < kIdxCap / kPass; ++ps) {
+      const int i0 = ps * kPass + 4 * tid;
+      if (i0 >= nblk * NKEY) continue;
+      int r[4] = {raw[ps].x, raw[ps].y, raw[ps].z, raw[ps].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = r[e];
+        const bool ok = (i0 + e < nslot) && t >= 0 && t < Lb;
+        if (validate && i0 + e < nslot) {
           if (!ok && t != -1) atomicOr(a.status, 1u);
           if (ok) {
             const uint32_t bit = 1u << (t & 31);
@@ -377,16 +439,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
             if (old & bit) atomicOr(a.status, 2u);
           }
         }
+        r[e] = ok ? t : -1;
       }
-      sidx[i] = row;
+      *reinterpret_cast<int4*>(sidx + i0) = make_int4(r[0], r[1], r[2], r[3]);
     }
-  } else if (validate) {
-    for (int i = tid; i < nslot; i += 256) {
-      const int t = s0 + i;
-      if (t < Lb) atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), 1u << (t & 31));
+  } else {
+    load_query();
+    if (validate) {
+      for (int i = tid; i < nslot; i += 256) {
+        const int t = s0 + i;
+        if (t < Lb) atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), 1u << (t & 31));
+      }
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   auto row_of = [&](int i) -> int {  // slot i of this split -> cache row or -1
@@ -711,7 +776,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 }  // namespace
 
 int launch_absorb(const AbsorbArgs& a, void* stream) {
-  hipLaunchKernelGGL(absorb_kernel, dim3(kHeads * 8), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(absorb_kernel, dim3(kHeads * 2), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
@@ -737,9 +802,9 @@ int launch_combine(const CombineArgs& a, void* stream) {
 
 int launch_value_up(const ValueUpArgs& a, void* stream) {
   if (a.o_latent == nullptr)
-    hipLaunchKernelGGL(value_up_kernel<true>, dim3(kHeads * 4), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(value_up_kernel<true>, dim3(kHeads), dim3(256), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL(value_up_kernel<false>, dim3(kHeads * 4), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(value_up_kernel<false>, dim3(kHeads), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
