@@ -52,3 +52,31 @@ def rowsum_dev(ref_scores: np.ndarray, lse_gpu: np.ndarray) -> float:
     (masked slots carry -inf and contribute 0)."""
     s = np.exp(ref_scores - lse_gpu[..., None])
     return float(np.max(np.abs(s.sum(-1) - 1.0)))
+
+
+def gather_rows_for_oracle(w, rows):
+    """Selected cache rows of sequences ``rows`` of a GPU-resident workload,
+    compacted on the host (plumbing: torch index_select, no arithmetic), with
+    the index lists remapped to 0..k-1.  Returns (kv, pe, lens, indices)."""
+    kvs, pes, idxs, lens = [], [], [], []
+    for b in rows:
+        Lb = int(w.seq_lens[b])
+        if w.indices is None:
+            pos = torch.arange(Lb, device=w.cache.device)
+            slot_pos = pos
+        else:
+            slot_pos = w.indices[b].long()
+            pos = slot_pos[slot_pos >= 0]
+        r = w.cache[b].index_select(0, pos).cpu()
+        kvs.append(r[:, : workload.DC])
+        pes.append(r[:, workload.DC:])
+        lens.append(r.shape[0])
+    k = max(lens)
+    kv = torch.zeros((len(rows), k, workload.DC), dtype=torch.bfloat16)
+    pe = torch.zeros((len(rows), k, workload.DR), dtype=torch.bfloat16)
+    idx = torch.full((len(rows), k), -1, dtype=torch.int64)
+    for i in range(len(rows)):
+        kv[i, : lens[i]] = kvs[i]
+        pe[i, : lens[i]] = pes[i]
+        idx[i, : lens[i]] = torch.arange(lens[i])
+    return kv, pe, torch.tensor(lens, dtype=torch.int32), idx

@@ -1,0 +1,133 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol that
+include/mla_decode.h declares, and rejects bad arguments on the host with the
+documented status codes before anything is enqueued (no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+LIB = os.path.join(ROOT, "sparse_mla_amd", "libmla_decode.so")
+
+OK, NULLP, BADDIM, ALIGN, WS, UNSUP, HIP, RANGE = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from sparse_mla_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    p, i32, i64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                 ctypes.c_float, ctypes.c_size_t)
+    L.mla_sparse_decode.argtypes = [p, p, i64, i64, p, i64, i64, p, i64, i64, p, i32, p, i32, f32, i32,
+                                    i32, i32, p, sz, p, p, u32, p, i64, p, p, p]
+    L.mla_absorb_q.argtypes = [p, i64, i64, p, p, i32, p]
+    L.mla_value_up.argtypes = [p, p, p, i64, i64, i32, p]
+    L.mla_combine.argtypes = [p, sz, i32, i32, p, p, p, p]
+    L.mla_combine_value_up.argtypes = [p, sz, i32, i32, p, p, i64, i64, p, p, p]
+    L.mla_dequant_wkv_b_fp8.argtypes = [p, p, p, p]
+    L.mla_workspace_bytes.restype = sz
+    L.mla_workspace_bytes.argtypes = [i32, i32]
+    L.mla_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.mla_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "mla_sparse_decode" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/mla_decode.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for code in range(8):
+        assert lib.mla_status_string(code)
+    assert lib.mla_last_hip_error() == 0
+
+
+def test_workspace_bytes(lib):
+    assert lib.mla_workspace_bytes(64, 1) == 0
+    assert lib.mla_workspace_bytes(64, 2) == 2 * 64 * 128 * (512 * 2 + 2 * 4)
+    assert lib.mla_workspace_bytes(0, 2) == 0 and lib.mla_workspace_bytes(4, 65) == 0
+
+
+def test_plan(lib):
+    s, g = ctypes.c_int32(), ctypes.c_int32()
+    for B, k, dense in [(1, 1001, 1), (32, 2048, 0), (64, 2048, 0), (128, 2048, 0), (64, 8192, 1), (7, 5000, 0)]:
+        assert lib.mla_plan(B, k, dense, 256, ctypes.byref(s), ctypes.byref(g)) == OK
+        assert 1 <= s.value <= 64 and g.value in (1, 2)
+        chunk = -(-(-(-k // s.value)) // (32 * g.value)) * 32 * g.value
+        if not dense:
+            assert chunk <= 2048
+    assert lib.mla_plan(0, 10, 0, 256, ctypes.byref(s), ctypes.byref(g)) == BADDIM
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address: never dereferenced (errors come first)
+
+
+def _decode(lib, **kw):
+    a = dict(q_abs=FAKE, q_pe=FAKE, q_pe_sb=128 * 64, q_pe_sh=64, kv=FAKE, kv_sb=576 * 100, kv_st=576,
+             pe=FAKE + 1024, pe_sb=576 * 100, pe_st=576, seq_lens=FAKE, max_len=100, indices=FAKE, k_max=64,
+             scale=0.07, B=2, S=1, HG=1, ws=None, ws_bytes=0, o_lat=FAKE, lse=None, flags=0, bitmap=None,
+             words=0, scores=None, status=None, stream=None)
+    a.update(kw)
+    return lib.mla_sparse_decode(a["q_abs"], a["q_pe"], a["q_pe_sb"], a["q_pe_sh"], a["kv"], a["kv_sb"],
+                                 a["kv_st"], a["pe"], a["pe_sb"], a["pe_st"], a["seq_lens"], a["max_len"],
+                                 a["indices"], a["k_max"], a["scale"], a["B"], a["S"], a["HG"], a["ws"],
+                                 a["ws_bytes"], a["o_lat"], a["lse"], a["flags"], a["bitmap"], a["words"],
+                                 a["scores"], a["status"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_abs=None), NULLP),
+    (dict(seq_lens=None), NULLP),
+    (dict(B=0), BADDIM),
+    (dict(k_max=0), BADDIM),
+    (dict(max_len=0), BADDIM),
+    (dict(S=0), BADDIM),
+    (dict(S=65), BADDIM),
+    (dict(HG=3), BADDIM),
+    (dict(indices=None, k_max=50), BADDIM),          # dense needs k_max >= max_len
+    (dict(k_max=4097, S=2, HG=1), BADDIM),            # > 2048 slots in one split
+    (dict(kv=FAKE + 8), ALIGN),
+    (dict(kv_st=580), ALIGN),
+    (dict(q_pe_sh=60), ALIGN),
+    (dict(kv_st=504, pe_st=504), UNSUP),
+    (dict(pe_st=56), UNSUP),
+    (dict(max_len=2000000, kv_sb=576 * 2000000, pe_sb=576 * 2000000), RANGE),
+    (dict(o_lat=None), NULLP),
+    (dict(S=2, ws=None), NULLP),
+    (dict(S=2, ws=FAKE, ws_bytes=100), WS),
+    (dict(flags=1), NULLP),                           # VALIDATE without bitmap/status
+    (dict(flags=1, bitmap=FAKE, status=FAKE, words=3), BADDIM),
+    (dict(flags=2), NULLP),                           # WRITE_SCORES without scores
+])
+def test_decode_rejects_bad_arguments(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_other_entry_points_reject_bad_arguments(lib):
+    assert lib.mla_absorb_q(None, 0, 0, FAKE, FAKE, 1, None) == NULLP
+    assert lib.mla_absorb_q(FAKE, 16384, 128, FAKE, FAKE, 0, None) == BADDIM
+    assert lib.mla_absorb_q(FAKE + 4, 16384, 128, FAKE, FAKE, 1, None) == ALIGN
+    assert lib.mla_absorb_q(FAKE, 16384, 127, FAKE, FAKE, 1, None) == ALIGN
+    assert lib.mla_value_up(FAKE, None, FAKE, 16384, 128, 1, None) == NULLP
+    assert lib.mla_value_up(FAKE, FAKE, FAKE, 16384, 128, 70000, None) == BADDIM
+    assert lib.mla_combine(None, 0, 4, 1, FAKE, None, None, None) == OK   # one split: no-op
+    assert lib.mla_combine(None, 0, 4, 2, FAKE, None, None, None) == NULLP
+    assert lib.mla_combine(FAKE, 10, 4, 2, FAKE, None, None, None) == WS
+    assert lib.mla_combine_value_up(FAKE, 1 << 30, 4, 1, FAKE, FAKE, 16384, 128, None, None, None) == BADDIM
+    assert lib.mla_combine_value_up(FAKE, 10, 4, 2, FAKE, FAKE, 16384, 128, None, None, None) == WS
+    assert lib.mla_dequant_wkv_b_fp8(None, FAKE, FAKE, None) == NULLP
+    assert lib.mla_dequant_wkv_b_fp8(FAKE + 2, FAKE, FAKE, None) == ALIGN
