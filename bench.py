@@ -35,6 +35,29 @@ ROTATION = {"dense_p1000_b1": 32, "sparse_b32_l4096_k2048": 10, "longctx_b64_k20
             "verylong_b128_l131072_k2048": 3, "dense_fp8w_b64_l8192": 2}
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "sparse_mla_amd", "csrc", "mla_kernels.hip")
+
+
+def counter_traffic(workload_name):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by a plain-copy calibration), or None when no
+    record exists for this workload or the kernel source changed since."""
+    import hashlib
+
+    path = os.path.join(HERE, "profiles", f"decode_kernel_counters_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return float(rec["decode_kernel_hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -264,7 +287,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": counter_traffic(name),
             "kernel": "mla_sparse_decode", "kernel_us": decode_ms * 1e3,
             "bytes_per_launch": dec_bytes, "mfma_tflops": dec_tflops,
             "mfma_frac": dec_tflops / BF16_PEAK_TFLOPS,
