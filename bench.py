@@ -70,7 +70,6 @@ def parse():
     ap.add_argument("--workload", default=None, help="workload name (default: the B=64, k=2048 long-context case)")
     ap.add_argument("--rotate", type=int, default=None, help="input sets cycled through (default per workload)")
     ap.add_argument("--splits", type=int, default=None)
-    ap.add_argument("--head-groups", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="sequences in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -183,7 +182,7 @@ def main():
     B = w0.B
     dense = w0.indices is None
     k_max = w0.k_max
-    bufs = mla.DecodeBuffers.allocate(B, k_max, dense, num_splits=args.splits, head_groups=args.head_groups)
+    bufs = mla.DecodeBuffers.allocate(B, k_max, dense, num_splits=args.splits)
     stream = torch.cuda.current_stream()
 
     def step(w, ev=None):
@@ -191,7 +190,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         mla.mla_sparse_decode(bufs.q_abs, w.q_pe, w.kv, w.pe, w.seq_lens, w.max_len, w.indices, w.scale,
-                              bufs.num_splits, bufs.head_groups, bufs.workspace, bufs.o_latent, bufs.lse,
+                              bufs.num_splits, bufs.workspace, bufs.o_latent, bufs.lse,
                               k_max=k_max)
         if ev is not None:
             ev[1].record(stream)
@@ -218,7 +217,7 @@ def main():
     ms_step = ms_total / args.steps
     decode_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     log(f"{args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us), "
-        f"decode kernel {decode_ms * 1e3:.2f} us; plan splits={bufs.num_splits} head_groups={bufs.head_groups}")
+        f"decode kernel {decode_ms * 1e3:.2f} us; plan splits={bufs.num_splits}")
 
     # Algorithmic work.
     if dense:
@@ -283,7 +282,7 @@ def main():
         "config": {
             "workload": name, "B": B, "k_max": k_max, "selected_keys": keys,
             "cache": f"[{B}, {spec.L}, 576] bf16 packed rows", "rotating_sets": R,
-            "num_splits": bufs.num_splits, "head_groups": bufs.head_groups,
+            "num_splits": bufs.num_splits,
         },
         "roofline": {
             "bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

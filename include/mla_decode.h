@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 #define MLA_HEADS 128
 #define MLA_NOPE_DIM 128
@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                     */
-  MLA_ERR_BAD_DIM = 2,             /* B, k_max, max_len, splits or head groups invalid */
+  MLA_ERR_BAD_DIM = 2,             /* B, k_max, max_len or splits invalid */
   MLA_ERR_ALIGNMENT = 3,           /* base not 16-byte aligned / stride not 8 elements */
   MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < mla_workspace_bytes(B, num_splits)   */
   MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths     */
@@ -83,14 +83,12 @@ const char* mla_status_string(int status);
 int mla_last_hip_error(void);
 
 /*
- * Launch plan for mla_sparse_decode: how many key splits per sequence and how
- * many head groups (1: a workgroup handles all 128 heads; 2: 64 heads each,
- * the two groups of one sequence share its gathered rows through L2).
+ * Launch plan for mla_sparse_decode: how many key splits per sequence (one
+ * workgroup per (sequence, split), each covering all 128 heads).
  * `dense` is nonzero when no index list is passed.  num_cus <= 0 means 256.
  * Pure host function.  Returns MLA_ERR_BAD_DIM for B < 1 or k_max < 1.
  */
-int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus,
-             int32_t* num_splits, int32_t* head_groups);
+int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus, int32_t* num_splits);
 
 /*
  * Bytes of workspace mla_sparse_decode needs for `num_splits` splits: 0 when
@@ -130,9 +128,9 @@ int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
  *            selects every t < L_b (dense decode; then k_max >= max_len).
  *   k_max    index slots per sequence.
  *   scale    softmax scale (qk_head_dim^-1/2 for this model).
- *   num_splits, head_groups   from mla_plan (1 <= S <= 64, groups 1 or 2).
- *            In sparse mode each split holds at most MLA_MAX_SLOTS_PER_SPLIT
- *            slots (ceil(k_max / S) rounded up to 32 * head_groups).
+ *   num_splits  from mla_plan (1 <= S <= 64).  Split s takes index slots
+ *            [s * chunk, (s + 1) * chunk), chunk = ceil(k_max / S) rounded up
+ *            to 32; in sparse mode chunk <= MLA_MAX_SLOTS_PER_SPLIT.
  *   workspace, ws_bytes       device scratch, >= mla_workspace_bytes(B, S);
  *            unused (may be NULL) when S == 1.
  *   o_latent bf16 [B][128][512], lse fp32 [B][128] (natural log; may be NULL):
@@ -155,8 +153,7 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
                       const void* pe, int64_t pe_sb, int64_t pe_st,
                       const int32_t* seq_lens, int32_t max_len,
                       const int32_t* indices, int32_t k_max, float scale, int32_t B,
-                      int32_t num_splits, int32_t head_groups,
-                      void* workspace, size_t ws_bytes,
+                      int32_t num_splits, void* workspace, size_t ws_bytes,
                       void* o_latent, float* lse,
                       uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
                       float* scores_out, uint32_t* status_dev, void* stream);

@@ -43,7 +43,7 @@ def _sig(name, res, args):
 _abi_version = _sig("mla_abi_version", ctypes.c_int, [])
 _status_string = _sig("mla_status_string", ctypes.c_char_p, [ctypes.c_int])
 _last_hip_error = _sig("mla_last_hip_error", ctypes.c_int, [])
-_plan = _sig("mla_plan", ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)])
+_plan = _sig("mla_plan", ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_i32)])
 _workspace_bytes = _sig("mla_workspace_bytes", _sz, [_i32, _i32])
 _absorb = _sig("mla_absorb_q", ctypes.c_int, [_p, _i64, _i64, _p, _p, _i32, _p])
 _decode = _sig("mla_sparse_decode", ctypes.c_int, [
@@ -52,8 +52,7 @@ _decode = _sig("mla_sparse_decode", ctypes.c_int, [
     _p, _i64, _i64,                # pe pe_sb pe_st
     _p, _i32,                      # seq_lens max_len
     _p, _i32, _f32, _i32,          # indices k_max scale B
-    _i32, _i32,                    # num_splits head_groups
-    _p, _sz,                       # workspace ws_bytes
+    _i32, _p, _sz,                 # num_splits workspace ws_bytes
     _p, _p,                        # o_latent lse
     _u32, _p, _i64,                # flags bitmap bitmap_words
     _p, _p, _p,                    # scores status stream
@@ -113,13 +112,13 @@ def mla_abi_version() -> int:
 
 
 def mla_plan(B: int, k_max: int, dense: bool, num_cus: Optional[int] = None):
-    """(num_splits, head_groups) for a launch."""
+    """Key splits per sequence for a launch."""
     if num_cus is None:
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count \
             if torch.cuda.is_available() else 256
-    s, g = _i32(), _i32()
-    _check("mla_plan", _plan(B, k_max, int(bool(dense)), num_cus, ctypes.byref(s), ctypes.byref(g)))
-    return s.value, g.value
+    s = _i32()
+    _check("mla_plan", _plan(B, k_max, int(bool(dense)), num_cus, ctypes.byref(s)))
+    return s.value
 
 
 def mla_workspace_bytes(B: int, num_splits: int) -> int:
@@ -145,7 +144,7 @@ def mla_absorb_q(q_nope: torch.Tensor, wkv_b: torch.Tensor, q_abs: Optional[torc
 
 
 def mla_sparse_decode(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indices, scale: float,
-                      num_splits: int, head_groups: int, workspace, o_latent, lse=None,
+                      num_splits: int, workspace, o_latent, lse=None,
                       flags: int = 0, bitmap=None, scores=None, status=None, k_max=None, stream=None):
     """kv [B, L, >=512 cols used as 512] and pe [B, L, 64] views (any strides with
     a unit last stride); indices int32 [B, k] or None (dense, k_max = max_len)."""
@@ -178,8 +177,7 @@ def mla_sparse_decode(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indices, scal
         _ptr(pe), pe.stride(0), pe.stride(1),
         _ptr(seq_lens), int(max_len),
         _ptr(indices), int(k_max), float(scale), B,
-        int(num_splits), int(head_groups),
-        _ptr(workspace), ws_bytes,
+        int(num_splits), _ptr(workspace), ws_bytes,
         _ptr(o_latent), _ptr(lse),
         int(flags), _ptr(bitmap), words,
         _ptr(scores), _ptr(status), _stream(stream)))
@@ -243,7 +241,6 @@ class DecodeBuffers:
     B: int
     k_max: int
     num_splits: int
-    head_groups: int
     q_abs: torch.Tensor
     o_latent: torch.Tensor
     lse: torch.Tensor
@@ -251,14 +248,12 @@ class DecodeBuffers:
     workspace: Optional[torch.Tensor]
 
     @staticmethod
-    def allocate(B: int, k_max: int, dense: bool, device="cuda", num_splits=None, head_groups=None):
-        if num_splits is None or head_groups is None:
-            s, g = mla_plan(B, k_max, dense)
-            num_splits = s if num_splits is None else num_splits
-            head_groups = g if head_groups is None else head_groups
+    def allocate(B: int, k_max: int, dense: bool, device="cuda", num_splits=None):
+        if num_splits is None:
+            num_splits = mla_plan(B, k_max, dense)
         ws = mla_workspace_bytes(B, num_splits)
         return DecodeBuffers(
-            B=B, k_max=k_max, num_splits=num_splits, head_groups=head_groups,
+            B=B, k_max=k_max, num_splits=num_splits,
             q_abs=torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=device),
             o_latent=torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=device),
             lse=torch.empty((B, HEADS), dtype=torch.float32, device=device),
@@ -274,7 +269,7 @@ def decode_step(bufs: DecodeBuffers, q_nope, q_pe, kv, pe, wkv_b, seq_lens, max_
     with fused, bufs.o_latent is not written when num_splits > 1)."""
     mla_absorb_q(q_nope, wkv_b, bufs.q_abs, stream=stream)
     mla_sparse_decode(bufs.q_abs, q_pe, kv, pe, seq_lens, max_len, indices, scale,
-                      bufs.num_splits, bufs.head_groups, bufs.workspace, bufs.o_latent, bufs.lse,
+                      bufs.num_splits, bufs.workspace, bufs.o_latent, bufs.lse,
                       flags=flags, bitmap=bitmap, scores=scores, status=status,
                       k_max=bufs.k_max, stream=stream)
     if bufs.num_splits > 1 and fused:

@@ -27,10 +27,7 @@ int hip_status(int err) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Index slots per split: ceil(k_max / S) rounded up to whole key blocks.
-int64_t split_chunk(int32_t k_max, int32_t S, int32_t head_groups) {
-  const int64_t blk = 32 * head_groups;
-  return ceil_div(ceil_div(k_max, S), blk) * blk;
-}
+int64_t split_chunk(int32_t k_max, int32_t S) { return ceil_div(ceil_div(k_max, S), 32) * 32; }
 
 }  // namespace
 
@@ -61,39 +58,33 @@ size_t mla_workspace_bytes(int32_t B, int32_t num_splits) {
   return units * MLA_LATENT_DIM * sizeof(uint16_t) + units * 2 * sizeof(float);
 }
 
-// Cost model (in nanoseconds) over head groups {1, 2} and splits 1..64:
-//  * compute: rounds of workgroups over the CUs times the keys each wave
-//    walks (a head-group-2 workgroup gives each wave half of its keys), at
-//    ~45 ns per key per wave (68 MFMA of 32x32x16 per 32 keys, ~60% busy);
-//  * partials: every extra split writes and re-reads a 128 x 512 bf16 mix
-//    per sequence, at ~5 TB/s.
+// Cost model (in nanoseconds) over splits 1..64, one workgroup per CU:
+//  * fixed: every round of workgroups loads its query tile and writes its
+//    normalised mix, ~14 us;
+//  * keys: ~68 ns per key slot of a split (a 32-key block of 68 MFMA
+//    32x32x16 per wave plus its gather, measured ~2.2 us);
+//  * partials: with S > 1 the mixes are re-read by the combine.
 // Sparse mode caps a split at MLA_MAX_SLOTS_PER_SPLIT slots.
-int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus,
-             int32_t* num_splits, int32_t* head_groups) {
-  if (B < 1 || k_max < 1 || !num_splits || !head_groups) return MLA_ERR_BAD_DIM;
+int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus, int32_t* num_splits) {
+  if (B < 1 || k_max < 1 || !num_splits) return MLA_ERR_BAD_DIM;
   if (num_cus <= 0) num_cus = 256;
   double best = 1e300;
-  int bs = 0, bg = 0;
-  for (int hg = 1; hg <= 2; ++hg) {
-    for (int S = 1; S <= MLA_MAX_SPLITS; ++S) {
-      const int64_t chunk = split_chunk(k_max, S, hg);
-      if (!dense && chunk > MLA_MAX_SLOTS_PER_SPLIT) continue;
-      if (S > 1 && (int64_t)(S - 1) * chunk >= k_max) break;  // an empty split
-      const int64_t wgs = (int64_t)B * S * hg;
-      const int64_t rounds = ceil_div(wgs, num_cus);
-      const double t_compute = (double)rounds * (double)(chunk / hg) * 45.0;
-      const double t_part = S > 1 ? (double)S * B * MLA_HEADS * MLA_LATENT_DIM * 2.0 * 2.0 / 5.0e3 : 0.0;
-      const double t = t_compute + t_part;
-      if (t < best * 0.999) {
-        best = t;
-        bs = S;
-        bg = hg;
-      }
+  int bs = 0;
+  for (int S = 1; S <= MLA_MAX_SPLITS; ++S) {
+    const int64_t chunk = split_chunk(k_max, S);
+    if (!dense && chunk > MLA_MAX_SLOTS_PER_SPLIT) continue;
+    if (S > 1 && (int64_t)(S - 1) * chunk >= k_max) break;  // an empty split
+    const int64_t rounds = ceil_div((int64_t)B * S, num_cus);
+    const double t_round = 14.0e3 + (double)chunk * 68.0;
+    const double t_part = S > 1 ? (double)S * B * MLA_HEADS * MLA_LATENT_DIM * 2.0 / 5.0e3 : 0.0;
+    const double t = (double)rounds * t_round + t_part;
+    if (t < best * 0.999) {
+      best = t;
+      bs = S;
     }
   }
   if (bs == 0) return MLA_ERR_BAD_DIM;
   *num_splits = bs;
-  *head_groups = bg;
   return MLA_OK;
 }
 
@@ -119,19 +110,17 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
                       const void* pe, int64_t pe_sb, int64_t pe_st,
                       const int32_t* seq_lens, int32_t max_len,
                       const int32_t* indices, int32_t k_max, float scale, int32_t B,
-                      int32_t num_splits, int32_t head_groups,
-                      void* workspace, size_t ws_bytes,
+                      int32_t num_splits, void* workspace, size_t ws_bytes,
                       void* o_latent, float* lse,
                       uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
                       float* scores_out, uint32_t* status_dev, void* stream) {
   if (!q_abs || !q_pe || !kv || !pe || !seq_lens) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536 || k_max < 1 || max_len < 1) return MLA_ERR_BAD_DIM;
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
-  if (head_groups != 1 && head_groups != 2) return MLA_ERR_BAD_DIM;
   if (!indices && k_max < max_len) return MLA_ERR_BAD_DIM;
-  const int64_t chunk = split_chunk(k_max, num_splits, head_groups);
+  const int64_t chunk = split_chunk(k_max, num_splits);
   if (indices && chunk > MLA_MAX_SLOTS_PER_SPLIT) return MLA_ERR_BAD_DIM;
-  if ((int64_t)B * num_splits * head_groups > (int64_t)1 << 30) return MLA_ERR_BAD_DIM;
+  if ((int64_t)B * num_splits > (int64_t)1 << 30) return MLA_ERR_BAD_DIM;
   if (!aligned16(q_abs) || !aligned16(q_pe) || !aligned16(kv) || !aligned16(pe) ||
       !stride8(q_pe_sb) || !stride8(q_pe_sh) || !stride8(kv_sb) || !stride8(kv_st) ||
       !stride8(pe_sb) || !stride8(pe_st))
@@ -186,7 +175,7 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
   a.bitmap_words = bitmap_words;
   a.scores = scores_out;
   a.status = status_dev;
-  return hip_status(mla::launch_decode(a, head_groups, stream));
+  return hip_status(mla::launch_decode(a, stream));
 }
 
 int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,

@@ -35,7 +35,7 @@ struct DecodeArgs {
   const int32_t* indices;   // NULL: dense
   int32_t max_len;
   int32_t k_max;
-  int32_t chunk;            // index slots per split (multiple of 32 * head groups)
+  int32_t chunk;            // index slots per split (multiple of 32)
   int32_t B;
   int32_t S;                // splits
   float scale;              // softmax scale
@@ -82,7 +82,7 @@ struct DequantArgs {
 
 // Each returns a hipError_t value (0 on success).
 int launch_absorb(const AbsorbArgs& a, void* stream);
-int launch_decode(const DecodeArgs& a, int head_groups, void* stream);
+int launch_decode(const DecodeArgs& a, void* stream);
 int launch_combine(const CombineArgs& a, void* stream);
 int launch_value_up(const ValueUpArgs& a, void* stream);  // fused combine when o_latent == NULL
 int launch_dequant(const DequantArgs& a, void* stream);

@@ -84,6 +84,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Score-chain MFMAs with the accumulator in VGPRs.  The kernels that use
+// them keep their big accumulators in AGPRs (AGPR-form compiler MFMAs), and a
+// compiler MFMA would put this chain there too.  Back-to-back accumulation
+// into the same registers needs no wait states; a VALU read of the result
+// does, so the last MFMA of a chain is mfma32_v_last.
+__device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
+  f32x16 c;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ void mfma32_v(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v_last(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(c)
+               : "v"(a), "v"(b));
+}
+
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -324,67 +343,75 @@ __global__ __launch_bounds__(256) void value_up_kernel(const ValueUpArgs a) {
 // ---------------------------------------------------------------------------
 // decode: sparse flash-decode over the selected cache rows.
 //
-// Workgroup = (sequence b, head group, key split); 4 waves.  With KL key lanes
-// (head_groups == KL), a workgroup covers 128 / KL heads as 4 / KL slices of
-// 32 heads; wave w = (slice w / KL, key lane w % KL).  Each block of
-// NKEY = 32 KL keys is gathered into LDS by buffer loads that write LDS
-// directly (16 bytes per lane, one 1 KiB line per instruction), NBUF blocks
-// in flight.  Masked slots get an offset past the record range, so their
-// rows arrive as zeros.
+// Workgroup = (sequence b, key split s), all 128 heads, 4 waves, one
+// workgroup per CU.  Keys are processed in blocks of 32.  Each block of rows
+// is gathered into LDS by buffer loads that write LDS directly (16 bytes per
+// lane; 8 adjacent lanes read one whole 128-byte line of one row); masked
+// slots get an offset past the record range, so their rows arrive as zeros.
 //
 // LDS block layout: a row [latent 512 | rotary 64] is 9 lines of 128 bytes
-// (8 chunks of 8 features each).  Line m of key k is the 128-byte segment
-// (m * NKEY + k) * 128, and chunk q of that line sits at 16-byte position
-// q ^ sw(k).  One gather instruction moves 8 segments (8 keys, one line
-// each): 8 adjacent lanes read one whole 128-byte line of one row.  sw() is
-// chosen so that the score reads (32 keys, one chunk) and the transpose
-// reads (8 keys x 4 chunks) hit distinct banks for 32- and 64-bank LDS.
+// (8 chunks of 8 features).  Line m of key k is the segment (m * 32 + k) * 128
+// and chunk q of that line sits at 16-byte position q ^ sw(k); sw() keeps the
+// score reads (32 keys, one chunk) and the transpose reads (4 keys x 4
+// chunks per 32 lanes) on distinct banks for 32- and 64-bank LDS.
 //
-// Per wave and block of 32 keys:
-//   scores  S^T[key][head] = sum_f row[key][f] Q~[head][f]: A = rows (LDS,
-//           ds_read_b128), B = [q~ | q_pe] (registers), M = keys, N = heads,
-//           36 MFMAs over the 576 features.
+// Work split per block (32 keys):
+//   scores  wave w, heads 32 w .. 32 w + 31: S^T[key][head] = sum_f row[key][f]
+//           Q~[head][f]; A = rows (LDS, ds_read_b128), B = [q~ | q_pe] of the
+//           wave's heads held in registers; M = keys, N = heads, 36 MFMAs.
 //   softmax each lane holds 16 keys of one head: in-lane max/sum plus one
-//           exchange with lane ^ 32; exp2 with the scale folded into log2 e.
-//   mix     O~^T[col][head] += sum_key C[key][col] P[head][key]: A = latent
-//           columns via transpose reads (M = 512 columns in 16 tiles), B = P
-//           taken from the score registers in place (K = keys, permuted
-//           consistently on both sides), N = heads.  Every accumulator of a
-//           lane belongs to its own head, so rescaling needs no exchange.
+//           exchange with lane ^ 32; exp2 with scale * log2 e folded in; lazy
+//           rescaling (the reference maximum moves only when a block exceeds
+//           it by 2^8).  P (bf16) goes to an LDS tile P[head][key].
+//   mix     wave w, latent columns 128 w .. 128 w + 127, all 128 heads:
+//           O~^T[col][head] += sum_key C^T[col][key] P^T[key][head]; A = C^T
+//           through transpose reads (4 column tiles), B = P^T from the LDS
+//           tile (4 head tiles); M = columns, N = heads, K = keys, 32 MFMAs.
+// Software pipeline: iteration j computes the scores of block j, then the
+// mix of block j - 1 interleaved with the softmax of block j; the barrier at
+// the top of each iteration both publishes P(j - 1) and marks the gather of
+// block j complete.  Three row buffers: j - 1 (mix), j (scores), j + 1
+// (gather in flight); P, rescale factors and flags are double-buffered.
 // ---------------------------------------------------------------------------
-template <int KL, int NBUF, bool DENSE>
+constexpr int kBlk = 32;                   // keys per block
+constexpr int kNbuf = 3;                   // row buffers
+constexpr int kBufBytes = 72 * kBlk * 16;  // 36864: one block of rows
+constexpr int kGpw = kBufBytes / 1024 / 4; // gather instructions per wave per block
+constexpr int kPRow = 80;                  // bytes per P row: 32 keys bf16 + 16 pad
+constexpr int kPBytes = kHeads * kPRow;    // one P tile
+constexpr int kOffP = kNbuf * kBufBytes;
+constexpr int kOffAlpha = kOffP + 2 * kPBytes;       // float [2][128]
+constexpr int kOffFlags = kOffAlpha + 2 * kHeads * 4; // int [2][4]
+constexpr int kOffStat = kOffFlags + 64;              // float [128] m, [128] l
+constexpr int kOffIdx = kOffStat + 2 * kHeads * 4;    // int [kIdxCap]
+constexpr int kDecodeLds = kOffIdx + kIdxCap * 4;
+
+template <bool DENSE>
 __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
-  constexpr int NKEY = 32 * KL;
-  constexpr int HPW = 128 / KL;                 // heads per workgroup
-  constexpr int BUF = 72 * NKEY * 16;           // bytes per block buffer
-  constexpr int GPW = BUF / 1024 / 4;           // gather instructions per wave per block
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * BUF + kIdxCap * 4];
+  __shared__ __attribute__((aligned(1024))) char smem[kDecodeLds];
   char LDS_AS* s3 = (char LDS_AS*)smem;
-  int* sidx = reinterpret_cast<int*>(smem + NBUF * BUF);
+  int* sidx = reinterpret_cast<int*>(smem + kOffIdx);
 
-  // Workgroup -> (sequence, split, head group).  Dispatch places workgroup i
-  // on XCD i % 8; the head groups of one (sequence, split) are given ids 8
-  // apart so they share an XCD (and its L2) and start together.
-  const int wg = blockIdx.x;
-  const int x8 = wg & 7, y = wg >> 3;
-  const int hg = y % KL;
-  const int unit = (y / KL) * 8 + x8;
-  if (unit >= a.B * a.S) return;
+  // Units (sequence, split) are numbered so that the splits of a sequence
+  // run on one XCD (workgroup x is dispatched to XCD x % 8): the sequence's
+  // query tile then comes from HBM once and from that XCD's L2 after.
+  const int units = a.B * a.S;
+  const int per_xcd = (units + 7) >> 3;
+  const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (unit >= units) return;
   const int b = unit / a.S, s = unit % a.S;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hs = wave / KL, kl = wave % KL;
   const int hh = lane >> 5;
-  const int head = hg * HPW + hs * 32 + (lane & 31);
+  const int head = 32 * wave + (lane & 31);   // this lane's head in the score/softmax phase
 
   constexpr bool dense = DENSE;
-  const bool validate = (a.flags & 1u) != 0 && hg == 0;
+  const bool validate = (a.flags & 1u) != 0;
   const int Lb = min(max(a.seq_lens[b], 0), a.max_len);
   const int s0 = s * a.chunk;
   const int s1 = min(a.k_max, s0 + a.chunk);
   const int nslot = max(0, s1 - s0);
-  const int nblk = (nslot + NKEY - 1) / NKEY;
+  const int nblk = (nslot + kBlk - 1) / kBlk;
 
   // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B layout.
   bf16x8 qf[36];
@@ -399,8 +426,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Stage this split's index slots as cache rows (-1 = masked).  The same
   // predicate decides validity, the attended bitmap and the device checks.
-  // Thread t owns slots 4 t .. 4 t + 3 of each 1024-slot pass; all of its
-  // loads are issued before any is used.
+  // Thread t owns slots 4 t .. 4 t + 3 of each 1024-slot pass; the query
+  // loads go out after the index loads and stay in flight while the indices
+  // are staged (vmcnt retires in order).
   if constexpr (!dense) {
     constexpr int kPass = 4 * 256;
     int4 raw[kIdxCap / kPass];
@@ -417,15 +445,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
         raw[ps].w = i0 + 3 < nslot ? a.indices[base + 3] : -1;
       }
     }
-    // The query operand loads go out after the index loads and stay in
-    // flight: vmcnt retires in order, so waiting for the indices leaves the
-    // 36 query loads outstanding, and the first block's wait covers them.
     load_query();
     asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
 #pragma unroll
     for (int ps = 0; ps < kIdxCap / kPass; ++ps) {
       const int i0 = ps * kPass + 4 * tid;
-      if (i0 >= nblk * NKEY) continue;
+      if (i0 >= nblk * kBlk) continue;
       int r[4] = {raw[ps].x, raw[ps].y, raw[ps].z, raw[ps].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -452,6 +477,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       }
     }
   }
+  int* flags = reinterpret_cast<int*>(smem + kOffFlags);
+  if (tid < 8) flags[tid] = 0;
   __syncthreads();
 
   auto row_of = [&](int i) -> int {  // slot i of this split -> cache row or -1
@@ -467,225 +494,312 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)b * a.pe_sb, (uint32_t)Lb * pe_rb);
   const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
 
-  // Gather block p into buffer p % NBUF.  Wave w moves key groups
-  // (8 keys each) KL*w .. KL*w+KL-1, all 9 lines; lane l takes key
-  // 8 * group + l / 8 and 16-byte position l % 8 of each line.
+  // Gather block p into buffer p % 3: wave w moves keys 8 w .. 8 w + 7, all
+  // 9 lines; lane l takes key 8 w + l / 8 and 16-byte position l % 8.
   auto issue = [&](int p) {
-    const uint32_t dst0 = lds0 + (uint32_t)((p % NBUF) * BUF);
+    const int key = 8 * wave + (lane >> 3);
+    const int row = row_of(p * kBlk + key);
+    const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz((uint32_t)key)) * 16u;
+    const uint32_t okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
+    const uint32_t ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
+    const uint32_t dst = lds0 + (uint32_t)((p % kNbuf) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
 #pragma unroll
-    for (int kg = 0; kg < KL; ++kg) {
-      const int key = 8 * (KL * wave + kg) + (lane >> 3);
-      const int row = row_of(p * NKEY + key);
-      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz((uint32_t)key)) * 16u;
-      const uint32_t okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
-      const uint32_t ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
-      const uint32_t dst = dst0 + (uint32_t)(8 * (KL * wave + kg)) * 128u;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) dma16(rkv, dst + (uint32_t)(m * NKEY * 128), okv + (uint32_t)(m * 128));
-      dma16(rpe, dst + (uint32_t)(8 * NKEY * 128), ope);
-    }
+    for (int m = 0; m < 8; ++m) dma16(rkv, dst + (uint32_t)(m * kBlk * 128), okv + (uint32_t)(m * 128));
+    dma16(rpe, dst + (uint32_t)(8 * kBlk * 128), ope);
   };
 
-  f32x16 acc[16];
-#pragma unroll
-  for (int ct = 0; ct < 16; ++ct) acc[ct] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
 
-  // Per-lane LDS offsets.  Score reads: key kl*32 + lane%32, chunk
-  // 2 st + hh (line st / 4, chunk-in-line 2 (st % 4) + hh).
+  // Score-read offsets: key lane % 32, chunk 2 st + hh (line st / 4).
   uint32_t qk_base[4];
   {
-    const uint32_t key = (uint32_t)(kl * 32 + (lane & 31));
+    const uint32_t key = (uint32_t)(lane & 31);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
       qk_base[s4] = key * 128u + (((uint32_t)(2 * s4 + hh)) ^ seg_swz(key)) * 16u;
   }
-  // Transpose reads: source lane i of group g reads key
-  // kl*32 + 16 ks + 8 r + 4 hh + i/4, columns 32 ct + 16 gm + 4 (i % 4):
-  // chunk-in-line 4 (ct % 2) + 2 gm + (i % 4) / 2, byte 8 (i % 2).
+  // Transpose-read offsets (mix A operand): source lane i of group g reads
+  // key 16 ks + 8 hh + 4 r + i / 4 (natural key order, matching the P tile
+  // read below) and columns 32 mt + 16 gm + 4 (i % 4) of the wave's quarter:
+  // line 2 w + mt / 2, chunk 4 (mt % 2) + 2 gm + (i % 4) / 2, byte 8 (i % 2).
   const int i16 = lane & 15, gm = (lane >> 4) & 1;
   uint32_t pc_base[2][2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c1 = 0; c1 < 2; ++c1) {
-      const uint32_t key = (uint32_t)(kl * 32 + 8 * r + 4 * hh + (i16 >> 2));
+      const uint32_t key = (uint32_t)(8 * hh + 4 * r + (i16 >> 2));
       const uint32_t q = (uint32_t)(4 * c1 + 2 * gm + ((i16 & 3) >> 1));
-      pc_base[r][c1] = key * 128u + ((q ^ seg_swz(key)) * 16u) + 8u * (uint32_t)(i16 & 1);
+      pc_base[r][c1] = (uint32_t)(2 * wave * kBlk * 128) + key * 128u + ((q ^ seg_swz(key)) * 16u) +
+                       8u * (uint32_t)(i16 & 1);
     }
+  // P tile: B operand of head 32 nt + lane % 32, keys 16 ks + 8 hh .. + 7.
+  uint32_t pr_base = (uint32_t)kOffP + (uint32_t)(lane & 31) * kPRow + 16u * (uint32_t)hh;
+  // P write: this lane's head row, keys 8 j + 4 hh .. + 3 for j = 0..3.
+  uint32_t pw_base = (uint32_t)kOffP + (uint32_t)head * kPRow + 8u * (uint32_t)hh;
 
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nblk) issue(p);
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
 
-  for (int j = 0; j < nblk; ++j) {
-    // Wait for block j: blocks j+1 .. j+NBUF-2 (when they exist) may stay in flight.
-    const int after = min(NBUF - 2, nblk - 1 - j);
-    if (NBUF >= 4 && after >= 2) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * GPW) : "memory");
-    } else if (NBUF >= 3 && after >= 1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GPW) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    if (j + NBUF - 1 < nblk) issue(j + NBUF - 1);
-
-    const char LDS_AS* buf = s3 + (j % NBUF) * BUF;
-
-    // Scores for this wave's 32 keys and 32 heads.  LDS reads run QK_AHEAD
-    // steps ahead of the MFMAs; the fences keep the scheduler from hoisting
-    // more (the query operand and the accumulators hold 400 registers).
-    f32x16 sacc = {};
-    {
-      constexpr int QK_AHEAD = 3;
-      bf16x8 ring[QK_AHEAD + 1];
-      auto qk_ld = [&](int st) {
-        const uint32_t off = qk_base[st & 3] + (uint32_t)((st >> 2) * NKEY * 128);
-        return *(const bf16x8 LDS_AS*)(buf + off);
-      };
+  // acc[..][nt] *= alpha of head 32 nt + lane % 32, on the accumulator
+  // registers in place (a C++ multiply would move all 256 accumulators into
+  // the VALU register file).  Only when some wave moved its reference max.
+  auto apply_rescale = [&](int pbuf) {
+    const int* fl = flags + 4 * pbuf;
+    if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
+    const float* al = reinterpret_cast<const float*>(smem + kOffAlpha) + kHeads * pbuf;
+    float alpha[4];
 #pragma unroll
-      for (int st = 0; st < QK_AHEAD; ++st) ring[st] = qk_ld(st);
+    for (int nt = 0; nt < 4; ++nt) alpha[nt] = al[32 * nt + (lane & 31)];
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-      for (int st = 0; st < 36; ++st) {
-        if (st + QK_AHEAD < 36) ring[(st + QK_AHEAD) % (QK_AHEAD + 1)] = qk_ld(st + QK_AHEAD);
-        sacc = mfma32(ring[st % (QK_AHEAD + 1)], qf[st], sacc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    const bool v_ok = row_of(j * NKEY + kl * 32 + (lane & 31)) >= 0;
-    const uint32_t vm = (uint32_t)__builtin_amdgcn_ballot_w64(v_ok);
-
-    float t[16];
-    float mloc = -INFINITY;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
-      t[v] = ((vm >> kloc) & 1u) ? sacc[v] * a.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, t[v]);
-    }
-    if (a.flags & 2u) {
-      float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * NKEY + kl * 32;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (j * NKEY + kl * 32 + kloc < nslot)
-          so[kloc] = ((vm >> kloc) & 1u) ? sacc[v] * a.scale : -INFINITY;
-      }
-    }
-    const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const bool need = mblk > m_run + kRescaleLog2;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float mnew = need ? mblk : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-      l_run *= alpha;
-      // acc *= alpha, on the accumulator registers in place: a plain C++
-      // multiply would move all 256 accumulators into the VALU register file.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float tmp;
           asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(acc[ct][v]), "=&v"(tmp)
-                       : "v"(alpha));
+                       : "+a"(acc[mt][nt][v]), "=&v"(tmp)
+                       : "v"(alpha[nt]));
         }
-      asm volatile("s_nop 3" ::: "memory");
-      m_run = mnew;
+    asm volatile("s_nop 3" ::: "memory");
+  };
+
+  // Mix of block p (its rows in buffer p % 3, its P tile in P buffer p % 2).
+  auto mix = [&](int p) {
+    const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
+    const char LDS_AS* pt = s3 + (p & 1) * kPBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 bp[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bp[nt] = *(const bf16x8 LDS_AS*)(pt + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
+        const bf16x8 av = tr_pair(buf + pc_base[0][mt & 1] + o, buf + pc_base[1][mt & 1] + o);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(av, bp[nt], acc[mt][nt]);
+      }
     }
+  };
+
+  // Scores of block j into sacc (this wave's 32 heads).
+  auto scores = [&](int j, f32x16& sacc) {
+    const char LDS_AS* buf = s3 + (j % kNbuf) * kBufBytes;
+    constexpr int QK_AHEAD = 2;
+    bf16x8 ring[QK_AHEAD + 1];
+    auto qk_ld = [&](int st) {
+      return *(const bf16x8 LDS_AS*)(buf + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
+    };
+#pragma unroll
+    for (int st = 0; st < QK_AHEAD; ++st) ring[st] = qk_ld(st);
+#pragma unroll
+    for (int st = 0; st < 36; ++st) {
+      if (st + QK_AHEAD < 36) ring[(st + QK_AHEAD) % (QK_AHEAD + 1)] = qk_ld(st + QK_AHEAD);
+      const bf16x8 kf = ring[st % (QK_AHEAD + 1)];
+      if (st == 0) sacc = mfma32_v_first(kf, qf[st]);
+      else if (st == 35) mfma32_v_last(sacc, kf, qf[st]);
+      else mfma32_v(sacc, kf, qf[st]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Scores of block j interleaved with the mix of block j - 1: slot k issues
+  // score MFMA k and mix MFMA k (k < 32), with every LDS operand read issued
+  // three or four slots before its MFMA so that LDS latency overlaps the
+  // matrix pipeline instead of stalling it.
+  auto scores_mix = [&](int j, f32x16& sacc) {
+    const char LDS_AS* kbuf = s3 + (j % kNbuf) * kBufBytes;
+    const int p = j - 1;
+    const char LDS_AS* vbuf = s3 + (p % kNbuf) * kBufBytes;
+    const char LDS_AS* pt = s3 + (p & 1) * kPBytes;
+    constexpr int AH = 3;
+    bf16x8 ring[AH + 1];
+    bf16x8 bp[4];  // k-step 0, then k-step 1 as each fragment's last use passes
+    bf16x8 av[2];
+    auto qk_ld = [&](int st) {
+      return *(const bf16x8 LDS_AS*)(kbuf + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
+    };
+    auto bp_ld = [&](int ks, int nt) {
+      return *(const bf16x8 LDS_AS*)(pt + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
+    };
+    auto av_ld = [&](int g) {  // group g = 4 ks + mt
+      const int ks = g >> 2, mt = g & 3;
+      const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
+      return tr_pair(vbuf + pc_base[0][mt & 1] + o, vbuf + pc_base[1][mt & 1] + o);
+    };
+#pragma unroll
+    for (int st = 0; st < AH; ++st) ring[st] = qk_ld(st);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) bp[nt] = bp_ld(0, nt);
+    av[0] = av_ld(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 36; ++k) {
+      if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
+      if (k < 28 && (k & 3) == 0) av[((k >> 2) + 1) & 1] = av_ld((k >> 2) + 1);
+      if (k >= 13 && k < 17) bp[k - 13] = bp_ld(1, k - 13);  // after slot 12 + nt
+      const bf16x8 kf = ring[k % (AH + 1)];
+      if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
+      else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
+      else mfma32_v(sacc, kf, qf[k]);
+      if (k < 32) {
+        const int ks = k >> 4, mt = (k >> 2) & 3, nt = k & 3;
+        (void)ks;
+        acc[mt][nt] = mfma32(av[(k >> 2) & 1], bp[nt], acc[mt][nt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax of block j (this lane: head `head`, 16 keys), then publish P(j)
+  // and the rescale factors of this wave's heads.
+  auto softmax = [&](int j, const f32x16& sacc) {
+    const bool v_ok = row_of(j * kBlk + (lane & 31)) >= 0;
+    const uint32_t vm = (uint32_t)__builtin_amdgcn_ballot_w64(v_ok);
+    const uint32_t vmh = vm >> (4 * hh);  // bit 8 (v / 4) + v % 4: key of sacc[v]
+    float t[16];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      t[v] = ((vmh >> (8 * (v >> 2) + (v & 3))) & 1u) ? sacc[v] * a.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, t[v]);
+    }
+    if (a.flags & 2u) {
+      float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * kBlk;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (j * kBlk + kloc < nslot) so[kloc] = ((vmh >> (8 * (v >> 2) + (v & 3))) & 1u) ? sacc[v] * a.scale : -INFINITY;
+      }
+    }
+    const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32));
+    // Move the reference max when this block exceeds it by more than 2^8; a
+    // head's accumulators are still zero while its max is -inf.
+    const bool need = mblk > m_run + kRescaleLog2;
+    const bool resc = need && m_run != -INFINITY;
+    const float mnew = need ? mblk : m_run;
+    const float alpha = resc ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+    l_run *= alpha;
+    m_run = mnew;
     const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-    bf16x8 pb0, pb1;
+    float pv[16];
     float lsum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(t[v] - mref);
-      lsum += p;
-      if (v < 8) pb0[v] = (__bf16)p;
-      else pb1[v - 8] = (__bf16)p;
+      pv[v] = __builtin_amdgcn_exp2f(t[v] - mref);
+      lsum += pv[v];
     }
     l_run += lsum;
+    char* pw = smem + (j & 1) * kPBytes + pw_base;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint2*>(pw + 16 * q) = pack4(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
+    const bool any = __builtin_amdgcn_ballot_w64(resc) != 0;
+    if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[kHeads * (j & 1) + head] = alpha;
+    if (lane == 0) flags[4 * (j & 1) + wave] = any ? 1 : 0;
+  };
 
-    // Mix the latents of this block into the accumulators (transpose reads
-    // PC_AHEAD MFMAs ahead, fenced as above).
-    {
-      constexpr int PC_AHEAD = 3;
-      bf16x8 ring[PC_AHEAD + 1];
-      auto pc_ld = [&](int i) {  // i = 2 ct + ks
-        const int ct = i >> 1, ks = i & 1;
-        const uint32_t o = (uint32_t)((ct >> 1) * NKEY * 128 + ks * 16 * 128);
-        return tr_pair(buf + pc_base[0][ct & 1] + o, buf + pc_base[1][ct & 1] + o);
-      };
+  // Wait for the gather of block j (the only loads in flight) and for every
+  // wave to finish the previous iteration (P, flags and rescale factors of
+  // block j - 1 are then visible, and buffer (j + 1) % 3 = (j - 2) % 3 is free).
+  auto sync_block = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (nblk > 0) issue(0);
+  // Resolve the query loads here, unconditionally, while the first gather is
+  // in flight: the operands then count as asm-defined, so no per-use vmcnt
+  // wait (which would also drain the in-order gathers) lands in the key loop.
 #pragma unroll
-      for (int i = 0; i < PC_AHEAD; ++i) ring[i] = pc_ld(i);
+  for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
+  if (nblk > 0) {
+    sync_block();
+    if (1 < nblk) issue(1);
+    f32x16 sacc = {};
+    scores(0, sacc);
+    softmax(0, sacc);
+  }
+  for (int j = 1; j < nblk; ++j) {
+    // Per-lane LDS bases are re-derived each iteration rather than kept as
+    // dozens of hoisted base + offset sums occupying registers.
+    asm volatile("" : "+v"(qk_base[0]), "+v"(qk_base[1]), "+v"(qk_base[2]), "+v"(qk_base[3]));
+    asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
+    asm volatile("" : "+v"(pr_base), "+v"(pw_base));
+    sync_block();
+    if (j + 1 < nblk) issue(j + 1);
+    apply_rescale((j - 1) & 1);
+    f32x16 sacc = {};
+    scores_mix(j, sacc);
+    softmax(j, sacc);
+  }
+  sync_block();
+  if (nblk > 0) {
+    apply_rescale((nblk - 1) & 1);
+    mix(nblk - 1);
+  }
+
+  // Per-head (max, sum): lanes l and l ^ 32 hold halves of the sum.
+  l_run += __shfl_xor(l_run, 32);
+  float* stat = reinterpret_cast<float*>(smem + kOffStat);
+  if (hh == 0) {
+    stat[head] = m_run;
+    stat[kHeads + head] = l_run;
+  }
+  __syncthreads();
+  float lh[4], mh[4];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if (i + PC_AHEAD < 32) ring[(i + PC_AHEAD) % (PC_AHEAD + 1)] = pc_ld(i + PC_AHEAD);
-        acc[i >> 1] = mfma32(ring[i % (PC_AHEAD + 1)], (i & 1) ? pb1 : pb0, acc[i >> 1]);
-        __builtin_amdgcn_sched_barrier(0);
+  for (int nt = 0; nt < 4; ++nt) {
+    mh[nt] = stat[32 * nt + (lane & 31)];
+    lh[nt] = stat[kHeads + 32 * nt + (lane & 31)];
+  }
+  // acc[mt][nt][v]: column 128 w + 32 mt + 8 (v / 4) + 4 hh + v % 4, head 32 nt + lane % 32.
+  // The normalised tile goes through LDS (the row buffers are free now) so
+  // that the global writes are whole 1 KB rows: tile row h holds head h's 512
+  // columns as 64 16-byte chunks, chunk c stored at position c ^ (h & 63).
+  uint16_t* dst = (a.S == 1) ? a.o_latent + (int64_t)b * kHeads * kLatent
+                             : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int hd = 32 * nt + (lane & 31);
+    // S == 1: an empty selection gives 0 * inf = NaN; a split with no key
+    // contributes nothing to the combine.
+    const float inv = (a.S == 1) ? 1.0f / lh[nt] : (lh[nt] > 0.f ? 1.0f / lh[nt] : 0.f);
+    char* trow = smem + hd * 1024 + 8 * hh;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = 16 * wave + 4 * mt + q4;
+        *reinterpret_cast<uint2*>(trow + ((c ^ (hd & 63)) << 4)) =
+            pack4(acc[mt][nt][4 * q4] * inv, acc[mt][nt][4 * q4 + 1] * inv, acc[mt][nt][4 * q4 + 2] * inv,
+                  acc[mt][nt][4 * q4 + 3] * inv);
+      }
+    if (wave == 0 && hh == 0) {
+      if (a.S == 1) {
+        if (a.lse != nullptr)
+          a.lse[(int64_t)b * kHeads + hd] = lh[nt] > 0.f ? (mh[nt] + __log2f(lh[nt])) * kLn2 : -INFINITY;
+        if (validate && hd == 0 && !(lh[nt] > 0.f)) atomicOr(a.status, 4u);
+      } else {
+        float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + hd) * 2;
+        pml[0] = mh[nt];
+        pml[1] = lh[nt];
       }
     }
   }
-
-  l_run += __shfl_xor(l_run, 32);
-
-  if constexpr (KL == 2) {
-    // Merge the two key lanes of each head slice through LDS.
-    __syncthreads();
-    float* mrg = reinterpret_cast<float*>(smem) + hs * (16 * 16 * 64 + 128);
-    if (kl == 1) {
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mrg[(ct * 16 + v) * 64 + lane] = acc[ct][v];
-      mrg[16384 + lane] = m_run;
-      mrg[16384 + 64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (kl == 0) {
-      const float m2 = mrg[16384 + lane], l2 = mrg[16384 + 64 + lane];
-      const float M = fmaxf(m_run, m2);
-      const float a1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-      const float a2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-      l_run = l_run * a1 + l2 * a2;
-      m_run = M;
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ct][v] = acc[ct][v] * a1 + mrg[(ct * 16 + v) * 64 + lane] * a2;
-    }
-  }
-  if (kl != 0) return;
-
-  if (a.S == 1) {
-    const float inv = 1.0f / l_run;  // empty selection: 0 * inf = NaN
-    uint16_t* o = a.o_latent + ((int64_t)b * kHeads + head) * kLatent + 4 * hh;
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<uint2*>(o + 32 * ct + 8 * q4) =
-            pack4(acc[ct][4 * q4] * inv, acc[ct][4 * q4 + 1] * inv, acc[ct][4 * q4 + 2] * inv,
-                  acc[ct][4 * q4 + 3] * inv);
-    if (a.lse != nullptr && hh == 0)
-      a.lse[(int64_t)b * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
-    if (validate && hs == 0 && lane == 0 && !(l_run > 0.f)) atomicOr(a.status, 4u);
-  } else {
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;  // an empty split contributes nothing
-    uint16_t* po = a.part_o + (((int64_t)s * a.B + b) * kHeads + head) * kLatent + 4 * hh;
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<uint2*>(po + 32 * ct + 8 * q4) =
-            pack4(acc[ct][4 * q4] * inv, acc[ct][4 * q4 + 1] * inv, acc[ct][4 * q4 + 2] * inv,
-                  acc[ct][4 * q4 + 3] * inv);
-    if (hh == 0) {
-      float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + head) * 2;
-      pml[0] = m_run;
-      pml[1] = l_run;
-    }
+  __syncthreads();
+  // Wave w copies rows w, w + 4, ...: lane l moves chunk l of the row.
+#pragma unroll 4
+  for (int h = wave; h < kHeads; h += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(smem + h * 1024 + ((lane ^ (h & 63)) << 4));
+    *reinterpret_cast<uint4*>(dst + (int64_t)h * kLatent + 8 * lane) = v;
   }
 }
 
@@ -780,18 +894,14 @@ int launch_absorb(const AbsorbArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_decode(const DecodeArgs& a, int head_groups, void* stream) {
-  const int units = a.B * a.S;
-  const int groups8 = (units + 7) / 8;
+int launch_decode(const DecodeArgs& a, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
-  const bool dense = a.indices == nullptr;
-  if (head_groups == 2) {
-    if (dense) hipLaunchKernelGGL((decode_kernel<2, 2, true>), dim3(groups8 * 16), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<2, 2, false>), dim3(groups8 * 16), dim3(256), 0, st, a);
-  } else {
-    if (dense) hipLaunchKernelGGL((decode_kernel<1, 4, true>), dim3(groups8 * 8), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<1, 4, false>), dim3(groups8 * 8), dim3(256), 0, st, a);
-  }
+  const int units = a.B * a.S;
+  const int grid = 8 * ((units + 7) / 8);  // whole XCD rounds; spare workgroups exit
+  if (a.indices == nullptr)
+    hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 

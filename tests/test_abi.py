@@ -23,7 +23,7 @@ def lib():
     p, i32, i64, u32, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                  ctypes.c_float, ctypes.c_size_t)
     L.mla_sparse_decode.argtypes = [p, p, i64, i64, p, i64, i64, p, i64, i64, p, i32, p, i32, f32, i32,
-                                    i32, i32, p, sz, p, p, u32, p, i64, p, p, p]
+                                    i32, p, sz, p, p, u32, p, i64, p, p, p]
     L.mla_absorb_q.argtypes = [p, i64, i64, p, p, i32, p]
     L.mla_value_up.argtypes = [p, p, p, i64, i64, i32, p]
     L.mla_combine.argtypes = [p, sz, i32, i32, p, p, p, p]
@@ -31,7 +31,7 @@ def lib():
     L.mla_dequant_wkv_b_fp8.argtypes = [p, p, p, p]
     L.mla_workspace_bytes.restype = sz
     L.mla_workspace_bytes.argtypes = [i32, i32]
-    L.mla_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.mla_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
     L.mla_status_string.restype = ctypes.c_char_p
     return L
 
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     for code in range(8):
         assert lib.mla_status_string(code)
     assert lib.mla_last_hip_error() == 0
@@ -63,14 +63,18 @@ def test_workspace_bytes(lib):
 
 
 def test_plan(lib):
-    s, g = ctypes.c_int32(), ctypes.c_int32()
+    s = ctypes.c_int32()
     for B, k, dense in [(1, 1001, 1), (32, 2048, 0), (64, 2048, 0), (128, 2048, 0), (64, 8192, 1), (7, 5000, 0)]:
-        assert lib.mla_plan(B, k, dense, 256, ctypes.byref(s), ctypes.byref(g)) == OK
-        assert 1 <= s.value <= 64 and g.value in (1, 2)
-        chunk = -(-(-(-k // s.value)) // (32 * g.value)) * 32 * g.value
+        assert lib.mla_plan(B, k, dense, 256, ctypes.byref(s)) == OK
+        assert 1 <= s.value <= 64
+        chunk = -(-(-(-k // s.value)) // 32) * 32
+        assert (s.value - 1) * chunk < k  # no empty split
         if not dense:
             assert chunk <= 2048
-    assert lib.mla_plan(0, 10, 0, 256, ctypes.byref(s), ctypes.byref(g)) == BADDIM
+    # The shapes the benchmark runs: one workgroup per CU where the keys allow.
+    for B, k, dense, want in [(64, 2048, 0, 4), (32, 2048, 0, 8)]:
+        assert lib.mla_plan(B, k, dense, 256, ctypes.byref(s)) == OK and s.value == want
+    assert lib.mla_plan(0, 10, 0, 256, ctypes.byref(s)) == BADDIM
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address: never dereferenced (errors come first)
@@ -79,12 +83,12 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address: never dereferenced (errors
 def _decode(lib, **kw):
     a = dict(q_abs=FAKE, q_pe=FAKE, q_pe_sb=128 * 64, q_pe_sh=64, kv=FAKE, kv_sb=576 * 100, kv_st=576,
              pe=FAKE + 1024, pe_sb=576 * 100, pe_st=576, seq_lens=FAKE, max_len=100, indices=FAKE, k_max=64,
-             scale=0.07, B=2, S=1, HG=1, ws=None, ws_bytes=0, o_lat=FAKE, lse=None, flags=0, bitmap=None,
+             scale=0.07, B=2, S=1, ws=None, ws_bytes=0, o_lat=FAKE, lse=None, flags=0, bitmap=None,
              words=0, scores=None, status=None, stream=None)
     a.update(kw)
     return lib.mla_sparse_decode(a["q_abs"], a["q_pe"], a["q_pe_sb"], a["q_pe_sh"], a["kv"], a["kv_sb"],
                                  a["kv_st"], a["pe"], a["pe_sb"], a["pe_st"], a["seq_lens"], a["max_len"],
-                                 a["indices"], a["k_max"], a["scale"], a["B"], a["S"], a["HG"], a["ws"],
+                                 a["indices"], a["k_max"], a["scale"], a["B"], a["S"], a["ws"],
                                  a["ws_bytes"], a["o_lat"], a["lse"], a["flags"], a["bitmap"], a["words"],
                                  a["scores"], a["status"], a["stream"])
 
@@ -97,9 +101,8 @@ def _decode(lib, **kw):
     (dict(max_len=0), BADDIM),
     (dict(S=0), BADDIM),
     (dict(S=65), BADDIM),
-    (dict(HG=3), BADDIM),
     (dict(indices=None, k_max=50), BADDIM),          # dense needs k_max >= max_len
-    (dict(k_max=4097, S=2, HG=1), BADDIM),            # > 2048 slots in one split
+    (dict(k_max=4097, S=2), BADDIM),                         # > 2048 slots in one split
     (dict(kv=FAKE + 8), ALIGN),
     (dict(kv_st=580), ALIGN),
     (dict(q_pe_sh=60), ALIGN),

@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, in the launch configuration that
-bench.py times (mla_plan's splits and head groups, combine fused into the
+bench.py times (mla_plan's splits, combine fused into the
 value-up launch), on sampled sequences the oracle computes one by one:
 outputs within 1e-2 * max|O_ref|, softmax rows summing to one within 1e-3
 (through the GPU's log-sum-exp), and the attended position set bit-exact."""
@@ -40,8 +40,8 @@ def test_full_size(mla, name):
     else:
         wkv_b = w.wkv_b.to(dev)
         wkv_b_ref = w.wkv_b
-    S, HG = mla.mla_plan(w.B, w.k_max, idx is None)
-    bufs = mla.DecodeBuffers.allocate(w.B, w.k_max, idx is None, num_splits=S, head_groups=HG)
+    S = mla.mla_plan(w.B, w.k_max, idx is None)
+    bufs = mla.DecodeBuffers.allocate(w.B, w.k_max, idx is None, num_splits=S)
     words = (w.max_len + 31) // 32
     bitmap = torch.zeros((w.B, words), dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)

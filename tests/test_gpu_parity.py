@@ -49,10 +49,10 @@ def test_value_up(mla):
     assert rel_err(f64(out)[:, 0], oracle.value_up(o_lat, w.wkv_b)) <= 4e-3
 
 
-def _run_decode(mla, g, S, HG, layout="packed", flags=0, bitmap=None, scores=None, status=None, fused=False):
+def _run_decode(mla, g, S, layout="packed", flags=0, bitmap=None, scores=None, status=None, fused=False):
     B = g.B
     k_max = g.k_max
-    bufs = mla.DecodeBuffers.allocate(B, k_max, g.indices is None, num_splits=S, head_groups=HG)
+    bufs = mla.DecodeBuffers.allocate(B, k_max, g.indices is None, num_splits=S)
     if layout == "packed":
         kv, pe = g.kv, g.pe
     else:  # two buffers, as in the pages' code
@@ -64,34 +64,34 @@ def _run_decode(mla, g, S, HG, layout="packed", flags=0, bitmap=None, scores=Non
 
 
 CASES = [
-    # (name, B, L, k, S, HG, layout)
-    ("sparse_b32_l4096_k2048", 3, 300, 100, 1, 1, "packed"),
-    ("sparse_b32_l4096_k2048", 3, 300, 100, 1, 2, "packed"),
-    ("sparse_b32_l4096_k2048", 3, 300, 100, 3, 2, "packed"),
-    ("sparse_b32_l4096_k2048", 3, 300, 100, 2, 1, "split"),
-    ("longctx_b64_k2048", 4, 3000, 700, 1, 1, "packed"),
-    ("longctx_b64_k2048", 4, 3000, 700, 2, 2, "split"),
-    ("longctx_b64_k2048", 4, 3000, 700, 5, 1, "packed"),
-    ("dense_p1000_b1", 2, 1001, None, 1, 2, "packed"),
-    ("dense_p1000_b1", 2, 1001, None, 4, 1, "split"),
+    # (name, B, L, k, S, layout)
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 1, "packed"),
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 3, "packed"),
+    ("sparse_b32_l4096_k2048", 3, 300, 100, 2, "split"),
+    ("sparse_b32_l4096_k2048", 9, 300, 100, 2, "packed"),   # B * S not a multiple of 8
+    ("longctx_b64_k2048", 4, 3000, 700, 1, "packed"),
+    ("longctx_b64_k2048", 4, 3000, 700, 2, "split"),
+    ("longctx_b64_k2048", 4, 3000, 700, 5, "packed"),
+    ("dense_p1000_b1", 2, 1001, None, 1, "packed"),
+    ("dense_p1000_b1", 2, 1001, None, 4, "split"),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-B{c[1]}-L{c[2]}-k{c[3]}-S{c[4]}-HG{c[5]}-{c[6]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-B{c[1]}-L{c[2]}-k{c[3]}-S{c[4]}-{c[5]}")
 def test_decode_small(mla, case):
-    name, B, L, k, S, HG, layout = case
+    name, B, L, k, S, layout = case
     w = workload.make(name, B=B, L=L, k=k)
     if w.indices is not None:
         w.indices[0, -7:] = -1          # padding slots in one row
     g = to_gpu(w)
-    bufs, out = _run_decode(mla, g, S, HG, layout)
+    bufs, out = _run_decode(mla, g, S, layout)
     ref = oracle_ref(w, want_weights=True)
     assert rel_err(f64(bufs.o_latent), ref["o_lat"]) <= REL_TOL
     assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
     assert rowsum_dev(ref["scores"], f64(bufs.lse)) <= ROWSUM_TOL
     if S > 1:  # combine fused into the value-up launch
         bufs.lse.fill_(float("nan"))
-        bufs2, out2 = _run_decode(mla, g, S, HG, layout, fused=True)
+        bufs2, out2 = _run_decode(mla, g, S, layout, fused=True)
         assert rel_err(f64(out2)[:, 0], ref["out"]) <= REL_TOL
         assert rowsum_dev(ref["scores"], f64(bufs2.lse)) <= ROWSUM_TOL
 
@@ -106,7 +106,7 @@ def test_decode_validate_bitmap_and_scores(mla):
     bitmap = torch.zeros((w.B, words), dtype=torch.int32, device="cuda")
     scores = torch.empty((w.B, 128, w.k_max), dtype=torch.float32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    bufs, out = _run_decode(mla, g, 2, 2, flags=mla.MLA_FLAG_VALIDATE | mla.MLA_FLAG_WRITE_SCORES,
+    bufs, out = _run_decode(mla, g, 2, flags=mla.MLA_FLAG_VALIDATE | mla.MLA_FLAG_WRITE_SCORES,
                             bitmap=bitmap, scores=scores, status=status)
     assert int(status.item()) == 0
     ref = oracle_ref(w, want_weights=True)
@@ -126,8 +126,8 @@ def test_decode_validate_bitmap_and_scores(mla):
     assert rowsum_dev(sc, f64(bufs.lse)) <= ROWSUM_TOL
 
 
-@pytest.mark.parametrize("S,HG,fused", [(1, 1, False), (2, 2, False), (2, 2, True)])
-def test_decode_validate_errors(mla, S, HG, fused):
+@pytest.mark.parametrize("S,fused", [(1, False), (2, False), (2, True)])
+def test_decode_validate_errors(mla, S, fused):
     """Out-of-range and repeated indices and an empty row set the status
     bits; the empty sequence yields NaN and the others stay finite."""
     w = workload.make("sparse_b32_l4096_k2048", B=3, L=200, k=64)
@@ -137,7 +137,7 @@ def test_decode_validate_errors(mla, S, HG, fused):
     g = to_gpu(w)
     bitmap = torch.zeros((w.B, 8), dtype=torch.int32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    bufs, out = _run_decode(mla, g, S, HG, flags=mla.MLA_FLAG_VALIDATE, bitmap=bitmap, status=status,
+    bufs, out = _run_decode(mla, g, S, flags=mla.MLA_FLAG_VALIDATE, bitmap=bitmap, status=status,
                             fused=fused)
     st = int(status.item())
     assert st == (mla.MLA_DEV_INDEX_OUT_OF_RANGE | mla.MLA_DEV_DUPLICATE_INDEX | mla.MLA_DEV_EMPTY_SELECTION)
@@ -158,12 +158,12 @@ def test_dequant_fp8_bit_exact(mla):
 def test_decode_deterministic_and_order_invariant(mla):
     w = workload.make("sparse_b32_l4096_k2048", B=4, L=1000, k=256)
     g = to_gpu(w)
-    _, out1 = _run_decode(mla, g, 2, 2)
+    _, out1 = _run_decode(mla, g, 2)
     o1 = out1.clone()
-    _, out2 = _run_decode(mla, g, 2, 2)
+    _, out2 = _run_decode(mla, g, 2)
     assert torch.equal(o1, out2)
     perm = torch.randperm(w.k_max, generator=torch.Generator().manual_seed(3))
     g.indices = g.indices[:, perm.cuda()].contiguous()
-    _, out3 = _run_decode(mla, g, 2, 2)
+    _, out3 = _run_decode(mla, g, 2)
     ref = oracle_ref(w)
     assert rel_err(f64(out3)[:, 0], ref["out"]) <= REL_TOL
