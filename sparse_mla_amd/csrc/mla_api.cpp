@@ -11,6 +11,8 @@
 
 #include "mla_kernels.h"
 
+static_assert(MLA_MAX_SLOTS_PER_SPLIT == mla::kIdxCap, "index staging capacity");
+
 namespace {
 
 thread_local int g_last_hip_error = 0;

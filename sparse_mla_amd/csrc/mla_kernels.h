@@ -13,7 +13,7 @@ constexpr int kRope = 64;
 constexpr int kLatent = 512;
 constexpr int kValue = 128;
 constexpr int kRowsPerHead = kNope + kValue;  // 256 rows of wkv_b per head
-constexpr int kIdxCap = 2048;                  // index slots staged per split
+constexpr int kIdxCap = 1024;                  // index slots staged per split
 
 struct AbsorbArgs {
   const uint16_t* q_nope;

@@ -367,24 +367,27 @@ __global__ __launch_bounds__(256) void value_up_kernel(const ValueUpArgs a) {
 //           O~^T[col][head] += sum_key C^T[col][key] P^T[key][head]; A = C^T
 //           through transpose reads (4 column tiles), B = P^T from the LDS
 //           tile (4 head tiles); M = columns, N = heads, K = keys, 32 MFMAs.
-// Software pipeline: iteration j computes the scores of block j, then the
-// mix of block j - 1 interleaved with the softmax of block j; the barrier at
-// the top of each iteration both publishes P(j - 1) and marks the gather of
-// block j complete.  Three row buffers: j - 1 (mix), j (scores), j + 1
-// (gather in flight); P, rescale factors and flags are double-buffered.
+// Software pipeline: iteration j runs the scores of block j interleaved
+// MFMA by MFMA with the mix of block j - 1, then the softmax of block j.
+// Four row buffers: j - 1 (mix), j (scores), j + 1 and j + 2 (gathers in
+// flight).  The barrier at the top of iteration j marks the gather of block j
+// complete and publishes P(j - 1); a second barrier inside the softmax keeps
+// P(j) from overwriting the single P tile before every wave has mixed j - 1.
 // ---------------------------------------------------------------------------
 constexpr int kBlk = 32;                   // keys per block
-constexpr int kNbuf = 3;                   // row buffers
+constexpr int kNbuf = 4;                   // row buffers
 constexpr int kBufBytes = 72 * kBlk * 16;  // 36864: one block of rows
 constexpr int kGpw = kBufBytes / 1024 / 4; // gather instructions per wave per block
 constexpr int kPRow = 80;                  // bytes per P row: 32 keys bf16 + 16 pad
 constexpr int kPBytes = kHeads * kPRow;    // one P tile
 constexpr int kOffP = kNbuf * kBufBytes;
-constexpr int kOffAlpha = kOffP + 2 * kPBytes;       // float [2][128]
-constexpr int kOffFlags = kOffAlpha + 2 * kHeads * 4; // int [2][4]
-constexpr int kOffStat = kOffFlags + 64;              // float [128] m, [128] l
-constexpr int kOffIdx = kOffStat + 2 * kHeads * 4;    // int [kIdxCap]
+constexpr int kOffAlpha = kOffP + kPBytes;            // float [128]
+constexpr int kOffFlags = kOffAlpha + kHeads * 4;     // int [4]
+constexpr int kOffIdx = kOffFlags + 64;               // int [kIdxCap]
+constexpr int kOffStat = kOffIdx;                     // float [128] m, [128] l: after the last gather
 constexpr int kDecodeLds = kOffIdx + kIdxCap * 4;
+static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
+static_assert(kHeads * 1024 <= kOffStat, "the epilogue tile must not reach the stats");
 
 template <bool DENSE>
 __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz((uint32_t)key)) * 16u;
     const uint32_t okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
     const uint32_t ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
-    const uint32_t dst = lds0 + (uint32_t)((p % kNbuf) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
+    const uint32_t dst = lds0 + (uint32_t)((p & (kNbuf - 1)) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
 #pragma unroll
     for (int m = 0; m < 8; ++m) dma16(rkv, dst + (uint32_t)(m * kBlk * 128), okv + (uint32_t)(m * 128));
     dma16(rpe, dst + (uint32_t)(8 * kBlk * 128), ope);
@@ -547,10 +550,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // acc[..][nt] *= alpha of head 32 nt + lane % 32, on the accumulator
   // registers in place (a C++ multiply would move all 256 accumulators into
   // the VALU register file).  Only when some wave moved its reference max.
-  auto apply_rescale = [&](int pbuf) {
-    const int* fl = flags + 4 * pbuf;
+  auto apply_rescale = [&]() {
+    const int* fl = flags;
     if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
-    const float* al = reinterpret_cast<const float*>(smem + kOffAlpha) + kHeads * pbuf;
+    const float* al = reinterpret_cast<const float*>(smem + kOffAlpha);
     float alpha[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) alpha[nt] = al[32 * nt + (lane & 31)];
@@ -571,8 +574,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Mix of block p (its rows in buffer p % 3, its P tile in P buffer p % 2).
   auto mix = [&](int p) {
-    const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
-    const char LDS_AS* pt = s3 + (p & 1) * kPBytes;
+    const char LDS_AS* buf = s3 + (p & (kNbuf - 1)) * kBufBytes;
+    const char LDS_AS* pt = s3;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 bp[4];
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Scores of block j into sacc (this wave's 32 heads).
   auto scores = [&](int j, f32x16& sacc) {
-    const char LDS_AS* buf = s3 + (j % kNbuf) * kBufBytes;
+    const char LDS_AS* buf = s3 + (j & (kNbuf - 1)) * kBufBytes;
     constexpr int QK_AHEAD = 2;
     bf16x8 ring[QK_AHEAD + 1];
     auto qk_ld = [&](int st) {
@@ -615,10 +618,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // three or four slots before its MFMA so that LDS latency overlaps the
   // matrix pipeline instead of stalling it.
   auto scores_mix = [&](int j, f32x16& sacc) {
-    const char LDS_AS* kbuf = s3 + (j % kNbuf) * kBufBytes;
+    const char LDS_AS* kbuf = s3 + (j & (kNbuf - 1)) * kBufBytes;
     const int p = j - 1;
-    const char LDS_AS* vbuf = s3 + (p % kNbuf) * kBufBytes;
-    const char LDS_AS* pt = s3 + (p & 1) * kPBytes;
+    const char LDS_AS* vbuf = s3 + (p & (kNbuf - 1)) * kBufBytes;
+    const char LDS_AS* pt = s3;
     constexpr int AH = 3;
     bf16x8 ring[AH + 1];
     bf16x8 bp[4];  // k-step 0, then k-step 1 as each fragment's last use passes
@@ -697,20 +700,26 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       lsum += pv[v];
     }
     l_run += lsum;
-    char* pw = smem + (j & 1) * kPBytes + pw_base;
+    // Every wave must be done mixing block j - 1 (reading the P tile, the
+    // rescale flags and factors) before they are overwritten.
+    if (j > 0) __syncthreads();
+    char* pw = smem + pw_base;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<uint2*>(pw + 16 * q) = pack4(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
     const bool any = __builtin_amdgcn_ballot_w64(resc) != 0;
-    if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[kHeads * (j & 1) + head] = alpha;
-    if (lane == 0) flags[4 * (j & 1) + wave] = any ? 1 : 0;
+    if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[head] = alpha;
+    if (lane == 0) flags[wave] = any ? 1 : 0;
   };
 
-  // Wait for the gather of block j (the only loads in flight) and for every
-  // wave to finish the previous iteration (P, flags and rescale factors of
-  // block j - 1 are then visible, and buffer (j + 1) % 3 = (j - 2) % 3 is free).
-  auto sync_block = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Wait for the gather of block j and for every wave to finish the previous
+  // iteration.  With `newer` the gather of block j + 1 (the 9 youngest
+  // memory instructions of this wave; vmcnt retires in order) stays in
+  // flight.
+  constexpr int kGatherOps = 9;  // issue(): 8 latent lines + 1 rotary line per lane
+  auto sync_block = [&](bool newer) {
+    if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGatherOps) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
@@ -721,8 +730,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
   if (nblk > 0) {
-    sync_block();
     if (1 < nblk) issue(1);
+    sync_block(1 < nblk);
+    if (2 < nblk) issue(2);
     f32x16 sacc = {};
     scores(0, sacc);
     softmax(0, sacc);
@@ -733,16 +743,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     asm volatile("" : "+v"(qk_base[0]), "+v"(qk_base[1]), "+v"(qk_base[2]), "+v"(qk_base[3]));
     asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
     asm volatile("" : "+v"(pr_base), "+v"(pw_base));
-    sync_block();
-    if (j + 1 < nblk) issue(j + 1);
-    apply_rescale((j - 1) & 1);
+    sync_block(j + 1 < nblk);
+    if (j + 2 < nblk) issue(j + 2);  // into buffer (j - 2) % 4, mixed last iteration
+    apply_rescale();
     f32x16 sacc = {};
     scores_mix(j, sacc);
     softmax(j, sacc);
   }
-  sync_block();
+  sync_block(false);
   if (nblk > 0) {
-    apply_rescale((nblk - 1) & 1);
+    apply_rescale();
     mix(nblk - 1);
   }
 

@@ -70,7 +70,7 @@ def test_plan(lib):
         chunk = -(-(-(-k // s.value)) // 32) * 32
         assert (s.value - 1) * chunk < k  # no empty split
         if not dense:
-            assert chunk <= 2048
+            assert chunk <= 1024
     # The shapes the benchmark runs: one workgroup per CU where the keys allow.
     for B, k, dense, want in [(64, 2048, 0, 4), (32, 2048, 0, 8)]:
         assert lib.mla_plan(B, k, dense, 256, ctypes.byref(s)) == OK and s.value == want
@@ -102,7 +102,7 @@ def _decode(lib, **kw):
     (dict(S=0), BADDIM),
     (dict(S=65), BADDIM),
     (dict(indices=None, k_max=50), BADDIM),          # dense needs k_max >= max_len
-    (dict(k_max=4097, S=2), BADDIM),                         # > 2048 slots in one split
+    (dict(k_max=2049, S=2), BADDIM),                         # > 1024 slots in one split
     (dict(kv=FAKE + 8), ALIGN),
     (dict(kv_st=580), ALIGN),
     (dict(q_pe_sh=60), ALIGN),
