@@ -223,121 +223,175 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
 
 // ---------------------------------------------------------------------------
 // value-up: out[b][h][d] = sum_c O~[b][h][c] W_UV,h[d][c]
-// Workgroup = head: 128 workgroups, each reading its 128 KB of W_UV once
-// (wave w keeps value rows 32 w .. 32 w + 31 in registers) and looping over
-// 32-row batch tiles.  Each O~ tile [32][512] is assembled in LDS (rows
-// padded to 1040 bytes, two buffers alternating), then wave w computes
-// value rows 32 w .. 32 w + 31: M = d (W_UV rows, contiguous along c, loaded
-// straight into registers while the tile is assembled), N = b (from LDS),
-// K = c.  FUSED: the tile is merged from the split partials of the decode
+// Workgroup = (head, tile of ROWS batch rows); the tiles of a head run on one
+// XCD, so W_UV,h (128 KB, held in registers: wave w keeps value rows
+// 32 w .. 32 w + 31) comes from HBM once and from L2 for the other tiles.
+// Wave w owns batch rows ROWS/4 * w .. of the tile: it gathers their latent
+// rows (one 1 KB row per LDS-DMA instruction, rows past B read as zeros) into
+// LDS slots of 1040 bytes, up to 4 splits per pass, and merges them in fp32
+// registers; no other wave touches those slots until the merged bf16 tile is
+// complete.  Then M = d (W_UV rows), N = b (tile rows from LDS), K = c.
+// FUSED: the rows are merged from the split partials of the decode
 // ("Softmax" page, normalisation over all selected keys):
 //   O~ = sum_s g_s O~_s, g_s = 2^(m_s - M) l_s / L, L = sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 (M + log2 L)
 // ---------------------------------------------------------------------------
-constexpr int kOtRow = 1040;  // bytes per O~ row in LDS (512 bf16 + 16 pad)
+constexpr int kOtRow = 1040;  // bytes per latent row in LDS (512 bf16 + 16 pad)
+constexpr int kVuSplits = 4;  // splits staged per pass
 
-template <bool FUSED>
-__global__ __launch_bounds__(256) void value_up_kernel(const ValueUpArgs a) {
-  __shared__ __attribute__((aligned(16))) char ot[2][32 * kOtRow];
-  const int h = blockIdx.x;
+template <bool FUSED, int ROWS>
+__global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
+  __shared__ __attribute__((aligned(1024))) char slots[kVuSplits * ROWS * kOtRow];
+  constexpr int RPW = ROWS / 4;  // batch rows per wave
+  const int ntiles = (a.B + ROWS - 1) / ROWS;
+  const int units = kHeads * ntiles;
+  const int per_xcd = (units + 7) >> 3;
+  const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (unit >= units) return;
+  const int h = unit / ntiles, b0 = (unit % ntiles) * ROWS;
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nrows = min(ROWS, a.B - b0);  // valid rows of the tile
+  const int r0 = RPW * wave;              // first tile row of this wave
+
   const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
   bf16x8 wf[32];
 #pragma unroll
   for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
 
-  const int nbt = (a.B + 31) / 32;
-  for (int bt = 0; bt < nbt; ++bt) {
-  char* tile = ot[bt & 1];
-  // O~ tile: wave w fills rows 8 w .. 8 w + 7; lane l owns columns
-  // 8 l .. 8 l + 7 of each row (one coalesced 1 KB line per load).  All loads
-  // of a pass are issued before any of them is used; rows past B read row
-  // B-1 and are written as zeros.
-  int64_t bh[8];
-  bool okr[8];
+  const int S = FUSED ? a.S : 1;
+  const int64_t sstride = (int64_t)a.B * kHeads;  // rows per split
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(char LDS_AS*)slots;
+  const int wave_rows = min(RPW, max(0, nrows - r0));  // rows of this wave that exist
+  // Gather splits c0 .. c0 + 3 of the wave's rows: one instruction per
+  // (split, row); lane l brings bytes 16 l .. of the row.  The record size
+  // stops at the wave's last valid row (later rows read as zeros).
+  auto gather = [&](int c0) {
+    const int nc = min(kVuSplits, S - c0);
+    for (int sc = 0; sc < nc; ++sc) {
+      const int64_t row0 = wave_rows > 0 ? (int64_t)(b0 + r0) * kHeads + h : 0;
+      const uint16_t* base = FUSED ? a.part_o + ((int64_t)(c0 + sc) * sstride + row0) * kLatent
+                                   : a.o_latent + row0 * kLatent;
+      const i32x4 rs = buffer_rsrc(base, wave_rows == 0 ? 0u : (uint32_t)(wave_rows - 1) * kHeads * kLatent * 2u + 1024u);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int bb = bt * 32 + 8 * wave + j;
-    okr[j] = bb < a.B;
-    bh[j] = (int64_t)min(bb, a.B - 1) * kHeads + h;
-  }
-  float v[8][8];
+      for (int j = 0; j < RPW; ++j)
+        dma16(rs, lds0 + (uint32_t)((sc * ROWS + r0 + j) * kOtRow),
+              (uint32_t)j * kHeads * kLatent * 2u + 16u * (uint32_t)lane);
+    }
+  };
+
+  // Merge weights: lane s loads split s's (max, sum) of each of the wave's
+  // rows before the first gather goes out; once everything has landed (one
+  // round trip) every lane reads them back with readlane and computes the
+  // same M and L, so no memory access or cross-lane exchange sits between the
+  // data and the merge.  S <= 64.
+  float v[RPW][8];
+  float Mx[RPW], iL[RPW];
+  float2 mlv[RPW];
   if constexpr (FUSED) {
-    // Lane s holds split s's (max, sum); the merge weights come from two wave
-    // reductions per row and are broadcast to all lanes.
-    const int64_t sstride = (int64_t)a.B * kHeads;
-    const int ls = min(lane, a.S - 1);
-    float2 ml[8];
+    const int ls = min(lane, S - 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      ml[j] = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)ls * sstride + bh[j]) * 2);
-    float g[8];
+    for (int j = 0; j < RPW; ++j) {
+      const int64_t bh = (int64_t)min(b0 + r0 + j, a.B - 1) * kHeads + h;
+      mlv[j] = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)ls * sstride + bh) * 2);
+    }
+  }
+  gather(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto lane_f = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+  if constexpr (FUSED) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float m = lane < a.S ? ml[j].x : -INFINITY;
-      float M = m;
+    for (int j = 0; j < RPW; ++j) {
+      float M = -INFINITY, L = 0.f;
+      if (S <= kVuSplits) {
+        // Straight-line form for the usual split counts: the rows' chains
+        // are independent (a runtime loop serialises readlane -> VALU).
+        float m[kVuSplits], l[kVuSplits];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-      const float e = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[j].y;
-      float L = e;
+        for (int sp = 0; sp < kVuSplits; ++sp) {
+          m[sp] = sp < S ? lane_f(mlv[j].x, sp) : -INFINITY;
+          l[sp] = lane_f(mlv[j].y, sp);
+          M = fmaxf(M, m[sp]);
+        }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-      g[j] = e / L;
+        for (int sp = 0; sp < kVuSplits; ++sp)
+          L += (m[sp] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[sp] - M) * l[sp];
+      } else {
+        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, lane_f(mlv[j].x, sp));
+        for (int sp = 0; sp < S; ++sp) {
+          const float m = lane_f(mlv[j].x, sp);
+          L += (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M) * lane_f(mlv[j].y, sp);
+        }
+      }
+      Mx[j] = M;
+      iL[j] = 1.0f / L;
       const float empty = L > 0.f ? 0.f : __builtin_nanf("");  // all -inf row: NaN, as in mla_combine
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[j][k] = empty;
-      if (lane == 0 && okr[j]) {
-        if (a.lse != nullptr) a.lse[bh[j]] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      if (lane == 0 && r0 + j < nrows) {
+        const int64_t bh = (int64_t)(b0 + r0 + j) * kHeads + h;
+        if (a.lse != nullptr) a.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         if (a.status != nullptr && h == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
       }
     }
-    for (int s0 = 0; s0 < a.S; s0 += 2) {
-      bf16x8 x[8][2];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          x[j][u] = ld8(a.part_o + ((int64_t)min(s0 + u, a.S - 1) * sstride + bh[j]) * kLatent + 8 * lane);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float gs = (s0 + u < a.S) ? __shfl(g[j], s0 + u) : 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[j][u][k];
-        }
-    }
   } else {
-    bf16x8 x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = ld8(a.o_latent + bh[j] * kLatent + 8 * lane);
+    for (int j = 0; j < RPW; ++j) {
+      Mx[j] = 0.f;
+      iL[j] = 1.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[j][k] = (float)x[j][k];
+      for (int k = 0; k < 8; ++k) v[j][k] = 0.f;
+    }
   }
+
+  for (int c0 = 0; c0 < S; c0 += kVuSplits) {
+    if (c0 > 0) {
+      // The previous pass's slot reads must be complete before its slots are
+      // gathered into again.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      gather(c0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const int nc = min(kVuSplits, S - c0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+    for (int sc = 0; sc < kVuSplits; ++sc) {
+      if (sc >= nc) break;
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        float gs = 1.f;
+        if constexpr (FUSED) {
+          const float m = lane_f(mlv[j].x, c0 + sc);
+          gs = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mx[j]) * lane_f(mlv[j].y, c0 + sc) * iL[j];
+        }
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + (sc * ROWS + r0 + j) * kOtRow + 16 * lane);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[k];
+      }
+    }
+  }
+  // Merged rows (bf16) into the split-0 slots; every wave's rows must be
+  // there before the products read the whole tile.
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
     bf16x8 y;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = okr[j] ? (__bf16)v[j][k] : (__bf16)0.f;
-    *reinterpret_cast<bf16x8*>(tile + (8 * wave + j) * kOtRow + 16 * lane) = y;
+    for (int k = 0; k < 8; ++k) y[k] = (__bf16)v[j][k];
+    *reinterpret_cast<bf16x8*>(slots + (r0 + j) * kOtRow + 16 * lane) = y;
   }
   __syncthreads();
 
+  // N = 32 tile rows; with ROWS = 16 the upper 16 columns are not written.
   f32x16 acc = {};
-  const char LDS_AS* ol = (const char LDS_AS*)tile + (lane & 31) * kOtRow + 16 * hh;
+  const char LDS_AS* ol = (const char LDS_AS*)slots + (lane & 31) * kOtRow + 16 * hh;
 #pragma unroll
   for (int st = 0; st < 32; ++st) acc = mfma32(wf[st], *(const bf16x8 LDS_AS*)(ol + 32 * st), acc);
-  const int bb = bt * 32 + (lane & 31);
-  if (bb < a.B) {
-    uint16_t* out = a.out + (int64_t)bb * a.out_sb + (int64_t)h * a.out_sh + 32 * wave + 4 * hh;
+  const int r = lane & 31;
+  if (r < nrows) {
+    uint16_t* out = a.out + (int64_t)(b0 + r) * a.out_sb + (int64_t)h * a.out_sh + 32 * wave + 4 * hh;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
       *reinterpret_cast<uint2*>(out + 8 * q4) = pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
   }
-  }  // batch tiles (two tile buffers: one barrier per tile suffices)
 }
 
 // ---------------------------------------------------------------------------
@@ -921,10 +975,19 @@ int launch_combine(const CombineArgs& a, void* stream) {
 }
 
 int launch_value_up(const ValueUpArgs& a, void* stream) {
-  if (a.o_latent == nullptr)
-    hipLaunchKernelGGL(value_up_kernel<true>, dim3(kHeads), dim3(256), 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL(value_up_kernel<false>, dim3(kHeads), dim3(256), 0, (hipStream_t)stream, a);
+  // 32-row tiles, or 16 when that is what it takes to give every CU a tile.
+  const bool small = a.B <= 32;
+  const int rows = small ? 16 : 32;
+  const int units = kHeads * ((a.B + rows - 1) / rows);
+  const dim3 grid(8 * ((units + 7) / 8));
+  const hipStream_t st = (hipStream_t)stream;
+  if (a.o_latent == nullptr) {
+    if (small) hipLaunchKernelGGL((value_up_kernel<true, 16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((value_up_kernel<true, 32>), grid, dim3(256), 0, st, a);
+  } else {
+    if (small) hipLaunchKernelGGL((value_up_kernel<false, 16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((value_up_kernel<false, 32>), grid, dim3(256), 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 
