@@ -197,26 +197,42 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
       }
       af[t][st] = tr_pair(wl + off[0], wl + off[1]);
     }
+  // The slab is in registers now; its LDS holds output tiles from here on:
+  // row r (batch row of the tile) = 512 bytes, 16-byte chunk c stored at
+  // position c ^ (r % 32), so that the global writes are whole row segments.
+  __syncthreads();
+  char* ot = wt;
   for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
     if (bt0 > 0) load_q(bt0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int bb = (bt0 + u) * 32 + (lane & 31);
       if (bt0 + u >= nbt) break;
       f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int st = 0; st < 8; ++st)
 #pragma unroll
         for (int t = 0; t < 2; ++t) acc[t] = mfma32(af[t][st], qb[u][st], acc[t]);
-      if (bb < a.B) {
-        uint16_t* o = a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + wave * 64 + 4 * hh;
+      // acc[t][v]: batch row lane % 32, column 64 w + 32 t + 8 (v / 4) + 4 hh + v % 4.
+      char* orow = ot + (lane & 31) * 512 + 8 * hh;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<uint2*>(o + 32 * t + 8 * q4) =
-                pack4(acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = 8 * wave + 4 * t + q4;
+          *reinterpret_cast<uint2*>(orow + ((c ^ (lane & 31)) << 4)) =
+              pack4(acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]);
+        }
+      __syncthreads();
+      // Thread t copies chunk t % 32 of rows t / 32 + 8 k.
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = (tid >> 5) + 8 * k, c = tid & 31;
+        const int bb = (bt0 + u) * 32 + r;
+        const uint4 val = *reinterpret_cast<const uint4*>(ot + r * 512 + ((c ^ r) << 4));
+        if (bb < a.B)
+          *reinterpret_cast<uint4*>(a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + 8 * c) = val;
       }
+      __syncthreads();
     }
   }
 }
