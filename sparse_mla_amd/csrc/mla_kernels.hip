@@ -554,6 +554,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   if (tid < 8) flags[tid] = 0;
   __syncthreads();
 
+  if (nblk == 0) {
+    // No slot in this split: the normalised mix is NaN with S == 1 (an empty
+    // selection) and 0 otherwise (the combine gives it no weight); the
+    // (max, sum) are (-inf, 0).  Everything below may then assume a block.
+    uint16_t* dst = (a.S == 1) ? a.o_latent + (int64_t)b * kHeads * kLatent
+                               : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
+    const uint32_t fb = (a.S == 1) ? 0x7fc07fc0u : 0u;
+    for (int i = tid; i < kHeads * kLatent / 8; i += 256)
+      reinterpret_cast<uint4*>(dst)[i] = uint4{fb, fb, fb, fb};
+    if (tid < kHeads) {
+      if (a.S == 1) {
+        if (a.lse != nullptr) a.lse[(int64_t)b * kHeads + tid] = -INFINITY;
+        if (validate && tid == 0) atomicOr(a.status, 4u);
+      } else {
+        float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + tid) * 2;
+        pml[0] = -INFINITY;
+        pml[1] = 0.f;
+      }
+    }
+    return;
+  }
+
   auto row_of = [&](int i) -> int {  // slot i of this split -> cache row or -1
     if constexpr (dense) {
       const int t = s0 + i;
@@ -793,16 +815,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     __syncthreads();
   };
 
-  if (nblk > 0) issue(0);
-  // Resolve the query loads here, unconditionally, while the first gather is
-  // in flight: the operands then count as asm-defined, so no per-use vmcnt
-  // wait (which would also drain the in-order gathers) lands in the key loop.
+  issue(0);
+  // Resolve the query loads here, while the first gather is in flight: the
+  // operands then count as asm-defined, so no per-use vmcnt wait (which would
+  // also drain the in-order gathers) lands in the key loop.
 #pragma unroll
   for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
-  if (nblk > 0) {
-    if (1 < nblk) issue(1);
-    sync_block(1 < nblk);
-    if (2 < nblk) issue(2);
+  if (1 < nblk) issue(1);
+  sync_block(1 < nblk);
+  if (2 < nblk) issue(2);
+  {
     f32x16 sacc = {};
     scores(0, sacc);
     softmax(0, sacc);
@@ -821,10 +843,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     softmax(j, sacc);
   }
   sync_block(false);
-  if (nblk > 0) {
-    apply_rescale();
-    mix(nblk - 1);
-  }
+  apply_rescale();
+  mix(nblk - 1);
 
   // Per-head (max, sum): lanes l and l ^ 32 hold halves of the sum.
   l_run += __shfl_xor(l_run, 32);

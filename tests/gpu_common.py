@@ -7,9 +7,10 @@ import torch
 import oracle
 from sparse_mla_amd import workload
 
-# the benchmark spec tolerance: max |O - O_ref| <= 1e-2 * max |O_ref| (the same bar is
+# Target tolerance: max |O - O_ref| <= 1e-2 * max |O_ref| (the same bar is
 # used for the absorbed query and the latent mix); softmax rows sum to one
-# within 1e-3.
+# within 1e-3 (checked on the kernel's own scores and LSE, with the LSE itself
+# held to the oracle's within lse_tol).
 REL_TOL = 1e-2
 ROWSUM_TOL = 1e-3
 
@@ -45,6 +46,51 @@ def oracle_ref(w: workload.Workload, rows=None, want_weights=False):
     return oracle.decode(w.q_nope.cpu()[sel], w.q_pe.cpu()[sel], cache[..., :workload.DC],
                          cache[..., workload.DC:], w.wkv_b.cpu(), w.seq_lens.cpu()[sel], idx, w.scale,
                          want_weights=want_weights, want_attended=True, att_len=cache.shape[1])
+
+
+def lse_bound(q_abs_ref, latents, scale: float) -> np.ndarray:
+    """Per-(row, head) bound on |LSE_gpu - LSE_ref|, from oracle quantities only.
+
+    The one rounding ahead of the scores is q~ to bf16 (the absorb output): a
+    round-to-nearest bf16 value errs by at most 2^-9 of its magnitude, so the
+    score of key t errs by at most scale * sum_c 2^-9 |q~_c| |c_t,c| (the
+    rotary half is exact bf16 input).  LSE is a smooth maximum of the scores
+    and moves by at most the largest score error.  The bound doubles that for
+    the kernel's fp32 accumulation and adds 1e-5 for the LSE arithmetic.
+    ``latents[i]`` holds the selected latent rows [n_i, 512] of row i."""
+    qa = np.abs(np.asarray(q_abs_ref, dtype=np.float64))  # [rows, H, 512]
+    tol = np.zeros(qa.shape[:2])
+    for i, c in enumerate(latents):
+        if len(c):
+            tol[i] = scale * 2.0 ** -8 * (qa[i] @ np.abs(np.asarray(c, dtype=np.float64)).T).max(axis=1)
+    return tol + 1e-5
+
+
+def selected_latents(w: workload.Workload, rows=None):
+    """The selected in-range latent rows of each sequence of a CPU-side workload."""
+    rows = list(range(w.B)) if rows is None else list(rows)
+    cache = w.cache.cpu()
+    out = []
+    for b in rows:
+        L = int(w.seq_lens[b])
+        if w.indices is None:
+            pos = np.arange(L)
+        else:
+            idx = w.indices.cpu()[b].numpy()
+            pos = np.unique(idx[(idx >= 0) & (idx < L)])
+        out.append(cache[b, torch.from_numpy(pos), :workload.DC].double().numpy())
+    return out
+
+
+def lse_tol(w: workload.Workload, ref, rows=None) -> np.ndarray:
+    return lse_bound(ref["q_abs"], selected_latents(w, rows), w.scale)
+
+
+def lse_dev(lse_gpu: np.ndarray, ref) -> np.ndarray:
+    """|LSE_gpu - LSE_ref| with equal infinities counting as zero."""
+    a, r = np.asarray(lse_gpu, dtype=np.float64), np.asarray(ref["lse"], dtype=np.float64)
+    same = (a == r)
+    return np.where(same, 0.0, np.abs(a - r))
 
 
 def rowsum_dev(ref_scores: np.ndarray, lse_gpu: np.ndarray) -> float:

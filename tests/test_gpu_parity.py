@@ -7,7 +7,8 @@ import torch
 
 import oracle
 from sparse_mla_amd import workload
-from tests.gpu_common import REL_TOL, ROWSUM_TOL, f64, oracle_ref, rel_err, rowsum_dev, to_gpu
+from tests.gpu_common import (REL_TOL, ROWSUM_TOL, f64, lse_dev, lse_tol, oracle_ref, rel_err, rowsum_dev,
+                              to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,7 @@ CASES = [
     ("sparse_b32_l4096_k2048", 3, 300, 100, 3, "packed"),
     ("sparse_b32_l4096_k2048", 3, 300, 100, 2, "split"),
     ("sparse_b32_l4096_k2048", 9, 300, 100, 2, "packed"),   # B * S not a multiple of 8
+    ("sparse_b32_l4096_k2048", 3, 300, 64, 3, "packed"),    # split 2 holds no slot
     ("longctx_b64_k2048", 4, 3000, 700, 1, "packed"),
     ("longctx_b64_k2048", 4, 3000, 700, 2, "split"),
     ("longctx_b64_k2048", 4, 3000, 700, 5, "packed"),
@@ -84,16 +86,22 @@ def test_decode_small(mla, case):
     if w.indices is not None:
         w.indices[0, -7:] = -1          # padding slots in one row
     g = to_gpu(w)
-    bufs, out = _run_decode(mla, g, S, layout)
+    k_max = w.max_len if w.indices is None else w.k_max
+    scores = torch.empty((w.B, 128, k_max), dtype=torch.float32, device="cuda")
+    bufs, out = _run_decode(mla, g, S, layout, flags=mla.MLA_FLAG_WRITE_SCORES, scores=scores)
     ref = oracle_ref(w, want_weights=True)
+    tol = lse_tol(w, ref)
     assert rel_err(f64(bufs.o_latent), ref["o_lat"]) <= REL_TOL
     assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
-    assert rowsum_dev(ref["scores"], f64(bufs.lse)) <= ROWSUM_TOL
+    assert np.all(lse_dev(f64(bufs.lse), ref) <= tol)
+    assert rowsum_dev(f64(scores), f64(bufs.lse)) <= ROWSUM_TOL
     if S > 1:  # combine fused into the value-up launch
         bufs.lse.fill_(float("nan"))
-        bufs2, out2 = _run_decode(mla, g, S, layout, fused=True)
+        bufs2, out2 = _run_decode(mla, g, S, layout, flags=mla.MLA_FLAG_WRITE_SCORES, scores=scores,
+                                  fused=True)
         assert rel_err(f64(out2)[:, 0], ref["out"]) <= REL_TOL
-        assert rowsum_dev(ref["scores"], f64(bufs2.lse)) <= ROWSUM_TOL
+        assert np.all(lse_dev(f64(bufs2.lse), ref) <= tol)
+        assert rowsum_dev(f64(scores), f64(bufs2.lse)) <= ROWSUM_TOL
 
 
 def test_decode_validate_bitmap_and_scores(mla):
