@@ -24,6 +24,8 @@
 // row-major tile, lane j receives column c0 + j of rows r0 .. r0 + 3: a
 // K-strided operand fragment.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <math.h>
 #include <stdint.h>
 
@@ -705,59 +707,82 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  // Scores of block j interleaved with the mix of block j - 1: slot k issues
-  // score MFMA k and mix MFMA k (k < 32), with every LDS operand read issued
-  // three or four slots before its MFMA so that LDS latency overlaps the
-  // matrix pipeline instead of stalling it.
-  auto scores_mix = [&](int j, f32x16& sacc) {
+  // Mix operands of block p (rows in buffer p % 4, P in the P tile): group
+  // g = 4 ks + mt is one transpose-read A fragment, used by 4 MFMAs (nt).
+  struct MixOps {
+    bf16x8 bp[4];  // P fragments of one k-step (nt)
+    bf16x8 av[2];  // A fragments of consecutive groups, alternating
+  };
+  auto bp_ld = [&](int ks, int nt) {
+    return *(const bf16x8 LDS_AS*)(s3 + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
+  };
+  auto av_ld = [&](int p, int g) {
+    const char LDS_AS* vbuf = s3 + (p & (kNbuf - 1)) * kBufBytes;
+    const int ks = g >> 2, mt = g & 3;
+    const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
+    return tr_pair(vbuf + pc_base[0][mt & 1] + o, vbuf + pc_base[1][mt & 1] + o);
+  };
+  auto mix_mfma = [&](MixOps& m, int g, int nt) {
+    acc[g & 3][nt] = mfma32(m.av[g & 1], m.bp[nt], acc[g & 3][nt]);
+  };
+
+  // Key-validity ballot of block j: bit k of the result = slot j * 32 + k
+  // holds a row.
+  auto valid_mask = [&](int j) -> uint32_t {
+    const bool v_ok = row_of(j * kBlk + (lane & 31)) >= 0;
+    return (uint32_t)__builtin_amdgcn_ballot_w64(v_ok);
+  };
+
+  // Scores of block j with the first half (k-step 0) of the mix of block
+  // j - 1: the 36 score MFMAs form one dependent chain, and the 16 mix MFMAs
+  // sit on its even slots, in the chain's latency shadow.  Every LDS operand
+  // is read three or more slots ahead.  On exit `m` holds the k-step 1 P
+  // fragments and the first k-step 1 A fragment.
+  auto scores_mix = [&](int j, f32x16& sacc, MixOps& m) {
     const char LDS_AS* kbuf = s3 + (j & (kNbuf - 1)) * kBufBytes;
     const int p = j - 1;
-    const char LDS_AS* vbuf = s3 + (p & (kNbuf - 1)) * kBufBytes;
-    const char LDS_AS* pt = s3;
     constexpr int AH = 3;
     bf16x8 ring[AH + 1];
-    bf16x8 bp[4];  // k-step 0, then k-step 1 as each fragment's last use passes
-    bf16x8 av[2];
     auto qk_ld = [&](int st) {
       return *(const bf16x8 LDS_AS*)(kbuf + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
-    };
-    auto bp_ld = [&](int ks, int nt) {
-      return *(const bf16x8 LDS_AS*)(pt + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
-    };
-    auto av_ld = [&](int g) {  // group g = 4 ks + mt
-      const int ks = g >> 2, mt = g & 3;
-      const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
-      return tr_pair(vbuf + pc_base[0][mt & 1] + o, vbuf + pc_base[1][mt & 1] + o);
     };
 #pragma unroll
     for (int st = 0; st < AH; ++st) ring[st] = qk_ld(st);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) bp[nt] = bp_ld(0, nt);
-    av[0] = av_ld(0);
+    for (int nt = 0; nt < 4; ++nt) m.bp[nt] = bp_ld(0, nt);
+    m.av[0] = av_ld(p, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
       if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
-      if (k < 28 && (k & 3) == 0) av[((k >> 2) + 1) & 1] = av_ld((k >> 2) + 1);
-      if (k >= 13 && k < 17) bp[k - 13] = bp_ld(1, k - 13);  // after slot 12 + nt
+      // Mix MFMA i = 4 g + nt (g = 0..3) runs in slot 2 i; A of group g + 1
+      // loads when group g starts, k-step 1's P once k-step 0's is used up.
+      if ((k & 7) == 0 && k < 32) m.av[((k >> 3) + 1) & 1] = av_ld(p, (k >> 3) + 1);
+      if (k >= 32) m.bp[k - 32] = bp_ld(1, k - 32);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
       else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
       else mfma32_v(sacc, kf, qf[k]);
-      if (k < 32) {
-        const int ks = k >> 4, mt = (k >> 2) & 3, nt = k & 3;
-        (void)ks;
-        acc[mt][nt] = mfma32(av[(k >> 2) & 1], bp[nt], acc[mt][nt]);
-      }
+      if ((k & 1) == 0 && k < 32) mix_mfma(m, k >> 3, (k >> 1) & 3);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Softmax of block j (this lane: head `head`, 16 keys), then publish P(j)
-  // and the rescale factors of this wave's heads.
-  auto softmax = [&](int j, const f32x16& sacc) {
-    const bool v_ok = row_of(j * kBlk + (lane & 31)) >= 0;
-    const uint32_t vm = (uint32_t)__builtin_amdgcn_ballot_w64(v_ok);
+  // and the rescale factors of this wave's heads.  With MIX, the second half
+  // (k-step 1, groups 4..7) of the mix of block j - 1 is spread over its
+  // stages, so the matrix pipe runs under the softmax's vector work.
+  auto softmax = [&](auto mix_tag, int j, const f32x16& sacc, uint32_t vm, MixOps& m) {
+    constexpr bool MIX = decltype(mix_tag)::value;
+    const int p = j - 1;
+    auto mix_group = [&](int g) {
+      if constexpr (MIX) {
+        if (g < 7) m.av[(g + 1) & 1] = av_ld(p, g + 1);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) mix_mfma(m, g, nt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
     const uint32_t vmh = vm >> (4 * hh);  // bit 8 (v / 4) + v % 4: key of sacc[v]
     float t[16];
     float mloc = -INFINITY;
@@ -766,6 +791,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       t[v] = ((vmh >> (8 * (v >> 2) + (v & 3))) & 1u) ? sacc[v] * a.scale_log2 : -INFINITY;
       mloc = fmaxf(mloc, t[v]);
     }
+    mix_group(4);
     if (a.flags & 2u) {
       float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * kBlk;
 #pragma unroll
@@ -784,21 +810,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     l_run *= alpha;
     m_run = mnew;
     const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-    float pv[16];
+    mix_group(5);
     float lsum = 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      pv[v] = __builtin_amdgcn_exp2f(t[v] - mref);
-      lsum += pv[v];
+    for (int v = 0; v < 8; ++v) {
+      t[v] = __builtin_amdgcn_exp2f(t[v] - mref);
+      lsum += t[v];
+    }
+    mix_group(6);
+#pragma unroll
+    for (int v = 8; v < 16; ++v) {
+      t[v] = __builtin_amdgcn_exp2f(t[v] - mref);
+      lsum += t[v];
     }
     l_run += lsum;
+    mix_group(7);
     // Every wave must be done mixing block j - 1 (reading the P tile, the
     // rescale flags and factors) before they are overwritten.
     if (j > 0) __syncthreads();
     char* pw = smem + pw_base;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint2*>(pw + 16 * q) = pack4(pv[4 * q], pv[4 * q + 1], pv[4 * q + 2], pv[4 * q + 3]);
+      *reinterpret_cast<uint2*>(pw + 16 * q) = pack4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
     const bool any = __builtin_amdgcn_ballot_w64(resc) != 0;
     if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[head] = alpha;
     if (lane == 0) flags[wave] = any ? 1 : 0;
@@ -826,8 +859,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   if (2 < nblk) issue(2);
   {
     f32x16 sacc = {};
+    MixOps m;
+    const uint32_t vm = valid_mask(0);
     scores(0, sacc);
-    softmax(0, sacc);
+    softmax(std::false_type{}, 0, sacc, vm, m);
   }
   for (int j = 1; j < nblk; ++j) {
     // Per-lane LDS bases are re-derived each iteration rather than kept as
@@ -838,9 +873,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     sync_block(j + 1 < nblk);
     if (j + 2 < nblk) issue(j + 2);  // into buffer (j - 2) % 4, mixed last iteration
     apply_rescale();
+    const uint32_t vm = valid_mask(j);
     f32x16 sacc = {};
-    scores_mix(j, sacc);
-    softmax(j, sacc);
+    MixOps m;
+    scores_mix(j, sacc, m);
+    softmax(std::true_type{}, j, sacc, vm, m);
   }
   sync_block(false);
   apply_rescale();
