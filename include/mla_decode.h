@@ -93,8 +93,10 @@ int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus, int32_t* 
 /*
  * Bytes of workspace mla_sparse_decode needs for `num_splits` splits: 0 when
  * num_splits == 1 (the normalised result is written directly), otherwise the
- * per-split normalised latent mixes, bf16 [S][B][128][512], followed by the
- * per-split (max in log2 units, sum) pairs, fp32 [S][B][128][2].
+ * per-split unnormalised latent sums sum_t 2^(u_t - m_s) c_t, bf16
+ * [S][B][128][512], followed by the per-split (m_s, l_s = sum_t 2^(u_t - m_s))
+ * pairs, fp32 [S][B][128][2]; u_t is the score in log2 units and m_s the
+ * split's reference maximum (within 8 of its largest u_t; -inf for no key).
  * Returns 0 for invalid arguments.
  */
 size_t mla_workspace_bytes(int32_t B, int32_t num_splits);

@@ -127,12 +127,15 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Four floats -> four bf16 (round to nearest even), packed for an 8-byte store.
+// Four floats -> four bf16 (round to nearest even), packed for an 8-byte
+// store; each pair is one two-input conversion.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  uint2 r;
-  r.x = (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
-  r.y = (uint32_t)bf16_bits(c) | ((uint32_t)bf16_bits(d) << 16);
-  return r;
+  return uint2{pack2(a, b), pack2(c, d)};
 }
 
 // ---------------------------------------------------------------------------
@@ -250,8 +253,9 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
 // registers; no other wave touches those slots until the merged bf16 tile is
 // complete.  Then M = d (W_UV rows), N = b (tile rows from LDS), K = c.
 // FUSED: the rows are merged from the split partials of the decode
-// ("Softmax" page, normalisation over all selected keys):
-//   O~ = sum_s g_s O~_s, g_s = 2^(m_s - M) l_s / L, L = sum_s 2^(m_s - M) l_s,
+// ("Softmax" page, normalisation over all selected keys), each the
+// unnormalised sum U_s of its split relative to its max m_s:
+//   O~ = sum_s g_s U_s, g_s = 2^(m_s - M) / L, L = sum_s 2^(m_s - M) l_s,
 //   lse = ln 2 (M + log2 L)
 // ---------------------------------------------------------------------------
 constexpr int kOtRow = 1040;  // bytes per latent row in LDS (512 bf16 + 16 pad)
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
         float gs = 1.f;
         if constexpr (FUSED) {
           const float m = lane_f(mlv[j].x, c0 + sc);
-          gs = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mx[j]) * lane_f(mlv[j].y, c0 + sc) * iL[j];
+          gs = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mx[j]) * iL[j];
         }
         const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + (sc * ROWS + r0 + j) * kOtRow + 16 * lane);
 #pragma unroll
@@ -558,8 +562,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   if (nblk == 0) {
     // No slot in this split: the normalised mix is NaN with S == 1 (an empty
-    // selection) and 0 otherwise (the combine gives it no weight); the
-    // (max, sum) are (-inf, 0).  Everything below may then assume a block.
+    // selection); with several splits the (unnormalised) sum is 0 and the
+    // merge gives it no weight.  (max, sum) = (-inf, 0).  Everything below
+    // may then assume a block.
     uint16_t* dst = (a.S == 1) ? a.o_latent + (int64_t)b * kHeads * kLatent
                                : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
     const uint32_t fb = (a.S == 1) ? 0x7fc07fc0u : 0u;
@@ -593,16 +598,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Gather block p into buffer p % 3: wave w moves keys 8 w .. 8 w + 7, all
   // 9 lines; lane l takes key 8 w + l / 8 and 16-byte position l % 8.
-  auto issue = [&](int p) {
+  // Blocks past the last one gather masked rows (zeros) into their buffer,
+  // which no remaining block uses; the line issue can then stay unconditional.
+  struct Gather {
+    uint32_t okv, ope, dst;
+  };
+  auto gather_setup = [&](int p) {
     const int key = 8 * wave + (lane >> 3);
-    const int row = row_of(p * kBlk + key);
+    const int row = p < nblk ? row_of(p * kBlk + key) : -1;
     const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz((uint32_t)key)) * 16u;
-    const uint32_t okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
-    const uint32_t ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
-    const uint32_t dst = lds0 + (uint32_t)((p & (kNbuf - 1)) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
+    Gather g;
+    g.okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
+    g.ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
+    g.dst = lds0 + (uint32_t)((p & (kNbuf - 1)) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
+    return g;
+  };
+  // Line m (0..7 latent, 8 rotary) of a block's gather.
+  auto gather_line = [&](const Gather& g, int m) {
+    if (m < 8) dma16(rkv, g.dst + (uint32_t)(m * kBlk * 128), g.okv + (uint32_t)(m * 128));
+    else dma16(rpe, g.dst + (uint32_t)(8 * kBlk * 128), g.ope);
+  };
+  auto issue = [&](int p) {
+    const Gather g = gather_setup(p);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) dma16(rkv, dst + (uint32_t)(m * kBlk * 128), okv + (uint32_t)(m * 128));
-    dma16(rpe, dst + (uint32_t)(8 * kBlk * 128), ope);
+    for (int m = 0; m < 9; ++m) gather_line(g, m);
   };
 
 
@@ -736,9 +755,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // Scores of block j with the first half (k-step 0) of the mix of block
   // j - 1: the 36 score MFMAs form one dependent chain, and the 16 mix MFMAs
   // sit on its even slots, in the chain's latency shadow.  Every LDS operand
-  // is read three or more slots ahead.  On exit `m` holds the k-step 1 P
-  // fragments and the first k-step 1 A fragment.
-  auto scores_mix = [&](int j, f32x16& sacc, MixOps& m) {
+  // is read three or more slots ahead.  The gather `gn` goes out one line
+  // every fourth slot: a burst of gathers from four waves backs up the CU's
+  // address unit and would stall the issuing wave's MFMAs.  On exit `m` holds
+  // the k-step 1 P fragments and the first k-step 1 A fragment.
+  auto scores_mix = [&](int j, f32x16& sacc, MixOps& m, const Gather& gn) {
     const char LDS_AS* kbuf = s3 + (j & (kNbuf - 1)) * kBufBytes;
     const int p = j - 1;
     constexpr int AH = 3;
@@ -759,6 +780,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       // loads when group g starts, k-step 1's P once k-step 0's is used up.
       if ((k & 7) == 0 && k < 32) m.av[((k >> 3) + 1) & 1] = av_ld(p, (k >> 3) + 1);
       if (k >= 32) m.bp[k - 32] = bp_ld(1, k - 32);
+      if ((k & 3) == 0) gather_line(gn, k >> 2);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
       else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
@@ -871,12 +893,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
     asm volatile("" : "+v"(pr_base), "+v"(pw_base));
     sync_block(j + 1 < nblk);
-    if (j + 2 < nblk) issue(j + 2);  // into buffer (j - 2) % 4, mixed last iteration
+    const Gather gn = gather_setup(j + 2);  // into buffer (j - 2) % 4, mixed last iteration
     apply_rescale();
     const uint32_t vm = valid_mask(j);
     f32x16 sacc = {};
     MixOps m;
-    scores_mix(j, sacc, m);
+    scores_mix(j, sacc, m, gn);
     softmax(std::true_type{}, j, sacc, vm, m);
   }
   sync_block(false);
@@ -898,27 +920,38 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     lh[nt] = stat[kHeads + 32 * nt + (lane & 31)];
   }
   // acc[mt][nt][v]: column 128 w + 32 mt + 8 (v / 4) + 4 hh + v % 4, head 32 nt + lane % 32.
-  // The normalised tile goes through LDS (the row buffers are free now) so
-  // that the global writes are whole 1 KB rows: tile row h holds head h's 512
-  // columns as 64 16-byte chunks, chunk c stored at position c ^ (h & 63).
+  // The tile goes through LDS (the row buffers are free now) so that the
+  // global writes are whole 1 KB rows: tile row h holds head h's 512 columns
+  // as 64 16-byte chunks, chunk c stored at position c ^ (h & 63).  With one
+  // split it is the normalised O~; with several, each split stores its
+  // unnormalised sum with (max, sum) and the merge applies 2^(m_s - M) / L.
   uint16_t* dst = (a.S == 1) ? a.o_latent + (int64_t)b * kHeads * kLatent
                              : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int hd = 32 * nt + (lane & 31);
-    // S == 1: an empty selection gives 0 * inf = NaN; a split with no key
-    // contributes nothing to the combine.
-    const float inv = (a.S == 1) ? 1.0f / lh[nt] : (lh[nt] > 0.f ? 1.0f / lh[nt] : 0.f);
     char* trow = smem + hd * 1024 + 8 * hh;
+    if (a.S == 1) {
+      const float inv = 1.0f / lh[nt];  // an empty selection gives 0 * inf = NaN
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c = 16 * wave + 4 * mt + q4;
-        *reinterpret_cast<uint2*>(trow + ((c ^ (hd & 63)) << 4)) =
-            pack4(acc[mt][nt][4 * q4] * inv, acc[mt][nt][4 * q4 + 1] * inv, acc[mt][nt][4 * q4 + 2] * inv,
-                  acc[mt][nt][4 * q4 + 3] * inv);
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = 16 * wave + 4 * mt + q4;
+          *reinterpret_cast<uint2*>(trow + ((c ^ (hd & 63)) << 4)) =
+              pack4(acc[mt][nt][4 * q4] * inv, acc[mt][nt][4 * q4 + 1] * inv, acc[mt][nt][4 * q4 + 2] * inv,
+                    acc[mt][nt][4 * q4 + 3] * inv);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c = 16 * wave + 4 * mt + q4;
+          *reinterpret_cast<uint2*>(trow + ((c ^ (hd & 63)) << 4)) =
+              pack4(acc[mt][nt][4 * q4], acc[mt][nt][4 * q4 + 1], acc[mt][nt][4 * q4 + 2], acc[mt][nt][4 * q4 + 3]);
+        }
+    }
     if (wave == 0 && hh == 0) {
       if (a.S == 1) {
         if (a.lse != nullptr)
@@ -941,7 +974,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: O~ = sum_s g_s O~_s, g_s = 2^(m_s - M) l_s / L, L = sum_s 2^(m_s - M) l_s
+// combine: O~ = sum_s g_s U_s, g_s = 2^(m_s - M) / L, L = sum_s 2^(m_s - M) l_s,
+// where U_s is split s's unnormalised sum (relative to its max m_s).
 // Workgroup = (sequence, 2 heads); each thread owns 4 latent columns.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
@@ -956,13 +990,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.S; ++s) {
     const float ms = a.part_ml[(s * stride_s + bh) * 2];
-    const float wl = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * a.part_ml[(s * stride_s + bh) * 2 + 1];
-    L += wl;
+    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    L += w * a.part_ml[(s * stride_s + bh) * 2 + 1];
     const uint2 v = *reinterpret_cast<const uint2*>(a.part_o + (s * stride_s + bh) * kLatent + col);
-    acc[0] += wl * __uint_as_float(v.x << 16);
-    acc[1] += wl * __uint_as_float(v.x & 0xffff0000u);
-    acc[2] += wl * __uint_as_float(v.y << 16);
-    acc[3] += wl * __uint_as_float(v.y & 0xffff0000u);
+    acc[0] += w * __uint_as_float(v.x << 16);
+    acc[1] += w * __uint_as_float(v.x & 0xffff0000u);
+    acc[2] += w * __uint_as_float(v.y << 16);
+    acc[3] += w * __uint_as_float(v.y & 0xffff0000u);
   }
   const float inv = 1.0f / L;
   *reinterpret_cast<uint2*>(a.o_latent + bh * kLatent + col) =
