@@ -75,7 +75,7 @@ int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus, int32_t* 
   for (int S = 1; S <= MLA_MAX_SPLITS; ++S) {
     const int64_t chunk = split_chunk(k_max, S);
     if (!dense && chunk > MLA_MAX_SLOTS_PER_SPLIT) continue;
-    if (S > 1 && (int64_t)(S - 1) * chunk >= k_max) break;  // an empty split
+    if (S > 1 && (int64_t)(S - 1) * chunk >= k_max) continue;  // an empty split (a larger S may fit again)
     const int64_t rounds = ceil_div((int64_t)B * S, num_cus);
     const double t_round = 14.0e3 + (double)chunk * 68.0;
     const double t_part = S > 1 ? (double)S * B * MLA_HEADS * MLA_LATENT_DIM * 2.0 / 5.0e3 : 0.0;

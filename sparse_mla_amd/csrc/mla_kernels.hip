@@ -762,7 +762,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   auto scores_mix = [&](int j, f32x16& sacc, MixOps& m, const Gather& gn) {
     const char LDS_AS* kbuf = s3 + (j & (kNbuf - 1)) * kBufBytes;
     const int p = j - 1;
-    constexpr int AH = 3;
+    constexpr int AH = 2;
+    f32x16 sodd;  // odd k-steps: a second chain halves the dependent latency
     bf16x8 ring[AH + 1];
     auto qk_ld = [&](int st) {
       return *(const bf16x8 LDS_AS*)(kbuf + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
@@ -783,11 +784,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       if ((k & 3) == 0) gather_line(gn, k >> 2);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
-      else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
+      else if (k == 1) sodd = mfma32_v_first(kf, qf[k]);
+      else if (k == 35) mfma32_v_last(sodd, kf, qf[k]);
+      else if (k & 1) mfma32_v(sodd, kf, qf[k]);
       else mfma32_v(sacc, kf, qf[k]);
       if ((k & 1) == 0 && k < 32) mix_mfma(m, k >> 3, (k >> 1) & 3);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // Step 34 (even chain) issued before step 35, whose wait states cover it.
+    sacc += sodd;
   };
 
   // Softmax of block j (this lane: head `head`, 16 keys), then publish P(j)

@@ -72,7 +72,7 @@ def test_plan(lib):
         if not dense:
             assert chunk <= 1024
     # The shapes the benchmark runs: one workgroup per CU where the keys allow.
-    for B, k, dense, want in [(64, 2048, 0, 4), (32, 2048, 0, 8)]:
+    for B, k, dense, want in [(64, 2048, 0, 4), (32, 2048, 0, 8), (1, 1001, 1, 32)]:
         assert lib.mla_plan(B, k, dense, 256, ctypes.byref(s)) == OK and s.value == want
     assert lib.mla_plan(0, 10, 0, 256, ctypes.byref(s)) == BADDIM
 
