@@ -444,21 +444,22 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 //           through transpose reads (4 column tiles), B = P^T from the LDS
 //           tile (4 head tiles); M = columns, N = heads, K = keys, 32 MFMAs.
 // Software pipeline: iteration j runs the scores of block j interleaved
-// MFMA by MFMA with the mix of block j - 1, then the softmax of block j.
-// Four row buffers: j - 1 (mix), j (scores), j + 1 and j + 2 (gathers in
-// flight).  The barrier at the top of iteration j marks the gather of block j
-// complete and publishes P(j - 1); a second barrier inside the softmax keeps
-// P(j) from overwriting the single P tile before every wave has mixed j - 1.
+// MFMA by MFMA with the first half of the mix of block j - 1, then the
+// softmax of block j with the second half of that mix under it, while the
+// gather of block j + 1 goes out line by line.  Three row buffers: j - 1
+// (mix), j (scores), j + 1 (gather in flight); P, the rescale factors and
+// flags are double-buffered, so the one barrier per block (top of iteration
+// j: gather j complete, P(j - 1) published, buffer j + 1 free) suffices.
 // ---------------------------------------------------------------------------
 constexpr int kBlk = 32;                   // keys per block
-constexpr int kNbuf = 4;                   // row buffers
+constexpr int kNbuf = 3;                   // row buffers
 constexpr int kBufBytes = 72 * kBlk * 16;  // 36864: one block of rows
 constexpr int kGpw = kBufBytes / 1024 / 4; // gather instructions per wave per block
 constexpr int kPRow = 80;                  // bytes per P row: 32 keys bf16 + 16 pad
 constexpr int kPBytes = kHeads * kPRow;    // one P tile
 constexpr int kOffP = kNbuf * kBufBytes;
-constexpr int kOffAlpha = kOffP + kPBytes;            // float [128]
-constexpr int kOffFlags = kOffAlpha + kHeads * 4;     // int [4]
+constexpr int kOffAlpha = kOffP + 2 * kPBytes;        // float [2][128]
+constexpr int kOffFlags = kOffAlpha + 2 * kHeads * 4; // int [2][4]
 constexpr int kOffIdx = kOffFlags + 64;               // int [kIdxCap]
 constexpr int kOffStat = kOffIdx;                     // float [128] m, [128] l: after the last gather
 constexpr int kDecodeLds = kOffIdx + kIdxCap * 4;
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     Gather g;
     g.okv = row >= 0 ? (uint32_t)row * kv_rb + q16 : kMaskedOffset;
     g.ope = row >= 0 ? (uint32_t)row * pe_rb + q16 : kMaskedOffset;
-    g.dst = lds0 + (uint32_t)((p & (kNbuf - 1)) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
+    g.dst = lds0 + (uint32_t)((p % kNbuf) * kBufBytes) + (uint32_t)(8 * wave) * 128u;
     return g;
   };
   // Line m (0..7 latent, 8 rotary) of a block's gather.
@@ -663,10 +664,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // acc[..][nt] *= alpha of head 32 nt + lane % 32, on the accumulator
   // registers in place (a C++ multiply would move all 256 accumulators into
   // the VALU register file).  Only when some wave moved its reference max.
-  auto apply_rescale = [&]() {
-    const int* fl = flags;
+  auto apply_rescale = [&](int pbuf) {
+    const int* fl = flags + 4 * pbuf;
     if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
-    const float* al = reinterpret_cast<const float*>(smem + kOffAlpha);
+    const float* al = reinterpret_cast<const float*>(smem + kOffAlpha) + kHeads * pbuf;
     float alpha[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) alpha[nt] = al[32 * nt + (lane & 31)];
@@ -687,8 +688,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Mix of block p (its rows in buffer p % 3, its P tile in P buffer p % 2).
   auto mix = [&](int p) {
-    const char LDS_AS* buf = s3 + (p & (kNbuf - 1)) * kBufBytes;
-    const char LDS_AS* pt = s3;
+    const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
+    const char LDS_AS* pt = s3 + (p & 1) * kPBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 bp[4];
@@ -707,7 +708,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Scores of block j into sacc (this wave's 32 heads).
   auto scores = [&](int j, f32x16& sacc) {
-    const char LDS_AS* buf = s3 + (j & (kNbuf - 1)) * kBufBytes;
+    const char LDS_AS* buf = s3 + (j % kNbuf) * kBufBytes;
     constexpr int QK_AHEAD = 2;
     bf16x8 ring[QK_AHEAD + 1];
     auto qk_ld = [&](int st) {
@@ -732,11 +733,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     bf16x8 bp[4];  // P fragments of one k-step (nt)
     bf16x8 av[2];  // A fragments of consecutive groups, alternating
   };
-  auto bp_ld = [&](int ks, int nt) {
-    return *(const bf16x8 LDS_AS*)(s3 + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
+  auto bp_ld = [&](int p, int ks, int nt) {
+    return *(const bf16x8 LDS_AS*)(s3 + (p & 1) * kPBytes + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
   };
   auto av_ld = [&](int p, int g) {
-    const char LDS_AS* vbuf = s3 + (p & (kNbuf - 1)) * kBufBytes;
+    const char LDS_AS* vbuf = s3 + (p % kNbuf) * kBufBytes;
     const int ks = g >> 2, mt = g & 3;
     const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
     return tr_pair(vbuf + pc_base[0][mt & 1] + o, vbuf + pc_base[1][mt & 1] + o);
@@ -760,10 +761,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // address unit and would stall the issuing wave's MFMAs.  On exit `m` holds
   // the k-step 1 P fragments and the first k-step 1 A fragment.
   auto scores_mix = [&](int j, f32x16& sacc, MixOps& m, const Gather& gn) {
-    const char LDS_AS* kbuf = s3 + (j & (kNbuf - 1)) * kBufBytes;
+    const char LDS_AS* kbuf = s3 + (j % kNbuf) * kBufBytes;
     const int p = j - 1;
-    constexpr int AH = 2;
-    f32x16 sodd;  // odd k-steps: a second chain halves the dependent latency
+    constexpr int AH = 3;
     bf16x8 ring[AH + 1];
     auto qk_ld = [&](int st) {
       return *(const bf16x8 LDS_AS*)(kbuf + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
@@ -771,7 +771,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int st = 0; st < AH; ++st) ring[st] = qk_ld(st);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) m.bp[nt] = bp_ld(0, nt);
+    for (int nt = 0; nt < 4; ++nt) m.bp[nt] = bp_ld(p, 0, nt);
     m.av[0] = av_ld(p, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -780,19 +780,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       // Mix MFMA i = 4 g + nt (g = 0..3) runs in slot 2 i; A of group g + 1
       // loads when group g starts, k-step 1's P once k-step 0's is used up.
       if ((k & 7) == 0 && k < 32) m.av[((k >> 3) + 1) & 1] = av_ld(p, (k >> 3) + 1);
-      if (k >= 32) m.bp[k - 32] = bp_ld(1, k - 32);
+      if (k >= 32) m.bp[k - 32] = bp_ld(p, 1, k - 32);
       if ((k & 3) == 0) gather_line(gn, k >> 2);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
-      else if (k == 1) sodd = mfma32_v_first(kf, qf[k]);
-      else if (k == 35) mfma32_v_last(sodd, kf, qf[k]);
-      else if (k & 1) mfma32_v(sodd, kf, qf[k]);
+      else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
       else mfma32_v(sacc, kf, qf[k]);
       if ((k & 1) == 0 && k < 32) mix_mfma(m, k >> 3, (k >> 1) & 3);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Step 34 (even chain) issued before step 35, whose wait states cover it.
-    sacc += sodd;
   };
 
   // Softmax of block j (this lane: head `head`, 16 keys), then publish P(j)
@@ -854,24 +850,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     mix_group(7);
     // Every wave must be done mixing block j - 1 (reading the P tile, the
     // rescale flags and factors) before they are overwritten.
-    if (j > 0) __syncthreads();
-    char* pw = smem + pw_base;
+    char* pw = smem + (j & 1) * kPBytes + pw_base;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<uint2*>(pw + 16 * q) = pack4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
     const bool any = __builtin_amdgcn_ballot_w64(resc) != 0;
-    if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[head] = alpha;
-    if (lane == 0) flags[wave] = any ? 1 : 0;
+    if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[kHeads * (j & 1) + head] = alpha;
+    if (lane == 0) flags[4 * (j & 1) + wave] = any ? 1 : 0;
   };
 
-  // Wait for the gather of block j and for every wave to finish the previous
-  // iteration.  With `newer` the gather of block j + 1 (the 9 youngest
-  // memory instructions of this wave; vmcnt retires in order) stays in
-  // flight.
-  constexpr int kGatherOps = 9;  // issue(): 8 latent lines + 1 rotary line per lane
-  auto sync_block = [&](bool newer) {
-    if (newer) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGatherOps) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Wait for the gather of block j (the only memory instructions in flight)
+  // and for every wave to finish the previous iteration.
+  auto sync_block = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
@@ -881,9 +872,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // also drain the in-order gathers) lands in the key loop.
 #pragma unroll
   for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
-  if (1 < nblk) issue(1);
-  sync_block(1 < nblk);
-  if (2 < nblk) issue(2);
+  sync_block();
+  issue(1);
   {
     f32x16 sacc = {};
     MixOps m;
@@ -897,17 +887,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     asm volatile("" : "+v"(qk_base[0]), "+v"(qk_base[1]), "+v"(qk_base[2]), "+v"(qk_base[3]));
     asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
     asm volatile("" : "+v"(pr_base), "+v"(pw_base));
-    sync_block(j + 1 < nblk);
-    const Gather gn = gather_setup(j + 2);  // into buffer (j - 2) % 4, mixed last iteration
-    apply_rescale();
+    sync_block();
+    const Gather gn = gather_setup(j + 1);  // into buffer (j - 2) % 3, mixed last iteration
+    apply_rescale((j - 1) & 1);
     const uint32_t vm = valid_mask(j);
     f32x16 sacc = {};
     MixOps m;
     scores_mix(j, sacc, m, gn);
     softmax(std::true_type{}, j, sacc, vm, m);
   }
-  sync_block(false);
-  apply_rescale();
+  sync_block();
+  apply_rescale((nblk - 1) & 1);
   mix(nblk - 1);
 
   // Per-head (max, sum): lanes l and l ^ 32 hold halves of the sum.
