@@ -177,6 +177,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
   auto load_q = [&](int bt0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      if (bt0 + u >= nbt) break;  // uniform: tiles past the batch are not loaded
       // Rows past B load row B-1: they only feed output columns that are
       // never stored, and unconditional loads keep all of them in flight.
       const int bb = min((bt0 + u) * 32 + (lane & 31), a.B - 1);
