@@ -88,9 +88,15 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // Score-chain MFMAs with the accumulator in VGPRs.  The kernels that use
 // them keep their big accumulators in AGPRs (AGPR-form compiler MFMAs), and a
-// compiler MFMA would put this chain there too.  Back-to-back accumulation
-// into the same registers needs no wait states; a VALU read of the result
-// does, so the last MFMA of a chain is mfma32_v_last.
+// compiler MFMA would put this chain there too.
+// Back-to-back accumulation into the same registers needs no wait states;
+// a vector read of the result does, so the last MFMA of a chain is
+// mfma32_v_last.  Inline asm hides the MFMA's latency from the compiler,
+// which takes the result as written when the statement ends: code around a
+// chain must give the compiler no reason to copy the accumulator between two
+// of its MFMAs (such a copy would read a sum still in flight).  Wait states
+// after every MFMA would rule that out, but they stall the wave's issue
+// behind the matrix pipe and roughly double the chain's time.
 __device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
   f32x16 c;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
@@ -430,44 +436,45 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 // (8 chunks of 8 features).  Line m of key k is the segment (m * 32 + k) * 128
 // and chunk q of that line sits at 16-byte position q ^ sw(k); sw() keeps the
 // score reads (32 keys, one chunk) and the transpose reads (4 keys x 4
-// chunks per 32 lanes) on distinct banks for 32- and 64-bank LDS.
+// chunks per 16 lanes) on distinct banks.
 //
-// Work split per block (32 keys):
-//   scores  wave w, heads 32 w .. 32 w + 31: S^T[key][head] = sum_f row[key][f]
-//           Q~[head][f]; A = rows (LDS, ds_read_b128), B = [q~ | q_pe] of the
-//           wave's heads held in registers; M = keys, N = heads, 36 MFMAs.
-//   softmax each lane holds 16 keys of one head: in-lane max/sum plus one
-//           exchange with lane ^ 32; exp2 with scale * log2 e folded in; lazy
-//           rescaling (the reference maximum moves only when a block exceeds
-//           it by 2^8).  P (bf16) goes to an LDS tile P[head][key].
-//   mix     wave w, latent columns 128 w .. 128 w + 127, all 128 heads:
-//           O~^T[col][head] += sum_key C^T[col][key] P^T[key][head]; A = C^T
-//           through transpose reads (4 column tiles), B = P^T from the LDS
-//           tile (4 head tiles); M = columns, N = heads, K = keys, 32 MFMAs.
-// Software pipeline: iteration j runs the scores of block j interleaved
-// MFMA by MFMA with the first half of the mix of block j - 1, then the
-// softmax of block j with the second half of that mix under it, while the
-// gather of block j + 1 goes out line by line.  Three row buffers: j - 1
-// (mix), j (scores), j + 1 (gather in flight); P, the rescale factors and
-// flags are double-buffered, so the one barrier per block (top of iteration
-// j: gather j complete, P(j - 1) published, buffer j + 1 free) suffices.
+// Wave w owns heads 32 w .. 32 w + 31 through the whole block:
+//   scores  S^T[key][head] = sum_f row[key][f] Q~[head][f]; A = rows (LDS,
+//           ds_read_b128), B = [q~ | q_pe] of the wave's heads held in
+//           registers; M = keys, N = heads; one dependent chain of 36 MFMAs.
+//   softmax each lane holds 16 keys of one head (lanes l and l ^ 32 share a
+//           head): in-lane max and sum plus one lane swap; exp2 with
+//           scale * log2 e folded in; lazy rescaling (the reference maximum
+//           moves only when a block exceeds it by 2^8).
+//   mix     O~^T[col][head] += sum_key C^T[col][key] P^T[key][head] over all
+//           512 columns; A = C^T through transpose reads, B = P straight from
+//           the softmax registers (the keys permuted alike in A and B);
+//           M = columns, N = heads, K = keys; 32 MFMAs.
+// P, the rescale decision and the running (max, sum) never leave the wave:
+// the only dependency between waves is the gathered block itself.
+//
+// Software pipeline, iteration j, after one barrier (block j has landed):
+//   A  the score chain of block j, with the softmax of block j - 1 spread
+//      over its slots (the vector work issues while each chain MFMA runs)
+//      and the gather of block j + 2 going out one line every fourth slot;
+//   B  the mix of block j - 1: 32 independent MFMAs.
+// Four row buffers: j - 1 (mix), j (scores), j + 1 and j + 2 (in flight).
+// Buffer (j + 2) % 4 last held block j - 2, mixed in iteration j - 1, which
+// every wave has finished before the barrier of iteration j.  Gathers past
+// the last block load masked rows (zeros) into their buffer, so exactly one
+// block (9 loads per wave) is always in flight behind the one waited for.
 // ---------------------------------------------------------------------------
-constexpr int kBlk = 32;                   // keys per block
-constexpr int kNbuf = 3;                   // row buffers
-constexpr int kBufBytes = 72 * kBlk * 16;  // 36864: one block of rows
-constexpr int kGpw = kBufBytes / 1024 / 4; // gather instructions per wave per block
-constexpr int kPRow = 80;                  // bytes per P row: 32 keys bf16 + 16 pad
-constexpr int kPBytes = kHeads * kPRow;    // one P tile
-constexpr int kOffP = kNbuf * kBufBytes;
-constexpr int kOffAlpha = kOffP + 2 * kPBytes;        // float [2][128]
-constexpr int kOffFlags = kOffAlpha + 2 * kHeads * 4; // int [2][4]
-constexpr int kOffIdx = kOffFlags + 64;               // int [kIdxCap]
-constexpr int kOffStat = kOffIdx;                     // float [128] m, [128] l: after the last gather
+constexpr int kBlk = 32;                    // keys per block
+constexpr int kNbuf = 4;                    // row buffers
+constexpr int kBufBytes = 72 * kBlk * 16;   // 36864: one block of rows
+constexpr int kOffIdx = kNbuf * kBufBytes;  // int [kIdxCap]
 constexpr int kDecodeLds = kOffIdx + kIdxCap * 4;
+constexpr int kSoftSteps = 17;              // softmax steps placed in the score chain
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
-static_assert(kHeads * 1024 <= kOffStat, "the epilogue tile must not reach the stats");
+static_assert(kHeads * 1024 <= kOffIdx, "the epilogue tile must stay inside the row buffers");
+static_assert(kSoftSteps < 36, "the softmax steps must fit the score chain");
 
-template <bool DENSE>
+template <bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kDecodeLds];
   char LDS_AS* s3 = (char LDS_AS*)smem;
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
-  const int head = 32 * wave + (lane & 31);   // this lane's head in the score/softmax phase
+  const int head = 32 * wave + (lane & 31);   // this lane's head throughout
 
   constexpr bool dense = DENSE;
   const bool validate = (a.flags & 1u) != 0;
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B layout.
   bf16x8 qf[36];
-  auto load_query = [&]() {
+  auto load_query = [&]() __attribute__((always_inline)) {
     const uint16_t* qa = a.q_abs + ((int64_t)b * kHeads + head) * kLatent + 8 * hh;
 #pragma unroll
     for (int st = 0; st < 32; ++st) qf[st] = ld8(qa + 16 * st);
@@ -558,22 +565,20 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       }
     }
   }
-  int* flags = reinterpret_cast<int*>(smem + kOffFlags);
-  if (tid < 8) flags[tid] = 0;
   __syncthreads();
 
+  uint16_t* dst = !SPLIT ? a.o_latent + (int64_t)b * kHeads * kLatent
+                             : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
   if (nblk == 0) {
     // No slot in this split: the normalised mix is NaN with S == 1 (an empty
     // selection); with several splits the (unnormalised) sum is 0 and the
     // merge gives it no weight.  (max, sum) = (-inf, 0).  Everything below
     // may then assume a block.
-    uint16_t* dst = (a.S == 1) ? a.o_latent + (int64_t)b * kHeads * kLatent
-                               : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
-    const uint32_t fb = (a.S == 1) ? 0x7fc07fc0u : 0u;
+    const uint32_t fb = !SPLIT ? 0x7fc07fc0u : 0u;
     for (int i = tid; i < kHeads * kLatent / 8; i += 256)
       reinterpret_cast<uint4*>(dst)[i] = uint4{fb, fb, fb, fb};
     if (tid < kHeads) {
-      if (a.S == 1) {
+      if constexpr (!SPLIT) {
         if (a.lse != nullptr) a.lse[(int64_t)b * kHeads + tid] = -INFINITY;
         if (validate && tid == 0) atomicOr(a.status, 4u);
       } else {
@@ -585,7 +590,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     return;
   }
 
-  auto row_of = [&](int i) -> int {  // slot i of this split -> cache row or -1
+  auto row_of = [&](int i) __attribute__((always_inline)) -> int {  // slot i of this split -> cache row or -1
     if constexpr (dense) {
       const int t = s0 + i;
       return (i < nslot && t < Lb) ? t : -1;
@@ -598,14 +603,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)b * a.pe_sb, (uint32_t)Lb * pe_rb);
   const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
 
-  // Gather block p into buffer p % 3: wave w moves keys 8 w .. 8 w + 7, all
+  // Gather block p into buffer p % 4: wave w moves keys 8 w .. 8 w + 7, all
   // 9 lines; lane l takes key 8 w + l / 8 and 16-byte position l % 8.
-  // Blocks past the last one gather masked rows (zeros) into their buffer,
-  // which no remaining block uses; the line issue can then stay unconditional.
   struct Gather {
     uint32_t okv, ope, dst;
   };
-  auto gather_setup = [&](int p) {
+  auto gather_setup = [&](int p) __attribute__((always_inline)) {
     const int key = 8 * wave + (lane >> 3);
     const int row = p < nblk ? row_of(p * kBlk + key) : -1;
     const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz((uint32_t)key)) * 16u;
@@ -616,16 +619,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     return g;
   };
   // Line m (0..7 latent, 8 rotary) of a block's gather.
-  auto gather_line = [&](const Gather& g, int m) {
+  auto gather_line = [&](const Gather& g, int m) __attribute__((always_inline)) {
     if (m < 8) dma16(rkv, g.dst + (uint32_t)(m * kBlk * 128), g.okv + (uint32_t)(m * 128));
     else dma16(rpe, g.dst + (uint32_t)(8 * kBlk * 128), g.ope);
   };
-  auto issue = [&](int p) {
+  auto issue = [&](int p) __attribute__((always_inline)) {
     const Gather g = gather_setup(p);
 #pragma unroll
     for (int m = 0; m < 9; ++m) gather_line(g, m);
   };
-
 
   // Score-read offsets: key lane % 32, chunk 2 st + hh (line st / 4).
   uint32_t qk_base[4];
@@ -635,135 +637,154 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     for (int s4 = 0; s4 < 4; ++s4)
       qk_base[s4] = key * 128u + (((uint32_t)(2 * s4 + hh)) ^ seg_swz(key)) * 16u;
   }
-  // Transpose-read offsets (mix A operand): source lane i of group g reads
-  // key 16 ks + 8 hh + 4 r + i / 4 (natural key order, matching the P tile
-  // read below) and columns 32 mt + 16 gm + 4 (i % 4) of the wave's quarter:
-  // line 2 w + mt / 2, chunk 4 (mt % 2) + 2 gm + (i % 4) / 2, byte 8 (i % 2).
+  // Transpose-read offsets (mix A operand, column tile mt, k-step ks): in
+  // each 16-lane group (gm = group & 1) source lane i reads key
+  // 16 ks + 8 r + 4 hh + i / 4 for the fragment's two reads r = 0, 1, and
+  // columns 32 mt + 16 gm + 4 (i % 4) .. + 3: line mt / 2, chunk
+  // 4 (mt % 2) + 2 gm + (i % 4) / 2, byte 8 (i % 2).  Output lane l then holds
+  // column 32 mt + l % 32 with key 16 ks + 8 r + 4 hh + e at k = 8 hh + 4 r + e,
+  // which is where the score layout leaves that key's P: the score
+  // accumulator element 8 ks + 4 r + e of lane l is key 16 ks + 8 r + 4 hh + e.
   const int i16 = lane & 15, gm = (lane >> 4) & 1;
   uint32_t pc_base[2][2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c1 = 0; c1 < 2; ++c1) {
-      const uint32_t key = (uint32_t)(8 * hh + 4 * r + (i16 >> 2));
+      const uint32_t key = (uint32_t)(8 * r + 4 * hh + (i16 >> 2));
       const uint32_t q = (uint32_t)(4 * c1 + 2 * gm + ((i16 & 3) >> 1));
-      pc_base[r][c1] = (uint32_t)(2 * wave * kBlk * 128) + key * 128u + ((q ^ seg_swz(key)) * 16u) +
-                       8u * (uint32_t)(i16 & 1);
+      pc_base[r][c1] = key * 128u + ((q ^ seg_swz(key)) * 16u) + 8u * (uint32_t)(i16 & 1);
     }
-  // P tile: B operand of head 32 nt + lane % 32, keys 16 ks + 8 hh .. + 7.
-  uint32_t pr_base = (uint32_t)kOffP + (uint32_t)(lane & 31) * kPRow + 16u * (uint32_t)hh;
-  // P write: this lane's head row, keys 8 j + 4 hh .. + 3 for j = 0..3.
-  uint32_t pw_base = (uint32_t)kOffP + (uint32_t)head * kPRow + 8u * (uint32_t)hh;
 
-  f32x16 acc[4][4];
+  // acc[mt][v]: column 32 mt + 8 (v / 4) + 4 hh + v % 4, head `head`.
+  f32x16 acc[16];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
+  for (int mt = 0; mt < 16; ++mt) acc[mt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // acc[..][nt] *= alpha of head 32 nt + lane % 32, on the accumulator
-  // registers in place (a C++ multiply would move all 256 accumulators into
-  // the VALU register file).  Only when some wave moved its reference max.
-  auto apply_rescale = [&](int pbuf) {
-    const int* fl = flags + 4 * pbuf;
-    if ((fl[0] | fl[1] | fl[2] | fl[3]) == 0) return;
-    const float* al = reinterpret_cast<const float*>(smem + kOffAlpha) + kHeads * pbuf;
-    float alpha[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) alpha[nt] = al[32 * nt + (lane & 31)];
+  // acc *= alpha (this lane's head) on the accumulator registers in place (a
+  // C++ multiply would move all 256 accumulators into vector registers).
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float tmp;
-          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(acc[mt][nt][v]), "=&v"(tmp)
-                       : "v"(alpha[nt]));
-        }
+      for (int v = 0; v < 16; ++v) {
+        float tmp;
+        asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                     : "+a"(acc[mt][v]), "=&v"(tmp)
+                     : "v"(alpha));
+      }
     asm volatile("s_nop 3" ::: "memory");
   };
 
-  // Mix of block p (its rows in buffer p % 3, its P tile in P buffer p % 2).
-  auto mix = [&](int p) {
+  // Mix of block p (rows in buffer p % 4) with this wave's P fragments pb[ks]:
+  // fragment i = 16 ks + mt, one MFMA each, A fragments read four ahead.
+  auto mix = [&](int p, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
     const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
-    const char LDS_AS* pt = s3 + (p & 1) * kPBytes;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 bp[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bp[nt] = *(const bf16x8 LDS_AS*)(pt + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
-        const bf16x8 av = tr_pair(buf + pc_base[0][mt & 1] + o, buf + pc_base[1][mt & 1] + o);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma32(av, bp[nt], acc[mt][nt]);
-      }
-    }
-  };
-
-  // Scores of block j into sacc (this wave's 32 heads).
-  auto scores = [&](int j, f32x16& sacc) {
-    const char LDS_AS* buf = s3 + (j % kNbuf) * kBufBytes;
-    constexpr int QK_AHEAD = 2;
-    bf16x8 ring[QK_AHEAD + 1];
-    auto qk_ld = [&](int st) {
-      return *(const bf16x8 LDS_AS*)(buf + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
+    auto av_ld = [&](int i) {
+      const int ks = i >> 4, mt = i & 15;
+      const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
+      return tr_pair(buf + pc_base[0][mt & 1] + o, buf + pc_base[1][mt & 1] + o);
     };
+    constexpr int MA = 4;
+    bf16x8 ring[MA + 1];
 #pragma unroll
-    for (int st = 0; st < QK_AHEAD; ++st) ring[st] = qk_ld(st);
+    for (int i = 0; i < MA; ++i) ring[i] = av_ld(i);
 #pragma unroll
-    for (int st = 0; st < 36; ++st) {
-      if (st + QK_AHEAD < 36) ring[(st + QK_AHEAD) % (QK_AHEAD + 1)] = qk_ld(st + QK_AHEAD);
-      const bf16x8 kf = ring[st % (QK_AHEAD + 1)];
-      if (st == 0) sacc = mfma32_v_first(kf, qf[st]);
-      else if (st == 35) mfma32_v_last(sacc, kf, qf[st]);
-      else mfma32_v(sacc, kf, qf[st]);
+    for (int i = 0; i < 32; ++i) {
+      if (i + MA < 32) ring[(i + MA) % (MA + 1)] = av_ld(i + MA);
+      acc[i & 15] = mfma32(ring[i % (MA + 1)], pb[i >> 4], acc[i & 15]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Mix operands of block p (rows in buffer p % 4, P in the P tile): group
-  // g = 4 ks + mt is one transpose-read A fragment, used by 4 MFMAs (nt).
-  struct MixOps {
-    bf16x8 bp[4];  // P fragments of one k-step (nt)
-    bf16x8 av[2];  // A fragments of consecutive groups, alternating
-  };
-  auto bp_ld = [&](int p, int ks, int nt) {
-    return *(const bf16x8 LDS_AS*)(s3 + (p & 1) * kPBytes + pr_base + (uint32_t)(32 * nt * kPRow + 32 * ks));
-  };
-  auto av_ld = [&](int p, int g) {
-    const char LDS_AS* vbuf = s3 + (p % kNbuf) * kBufBytes;
-    const int ks = g >> 2, mt = g & 3;
-    const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
-    return tr_pair(vbuf + pc_base[0][mt & 1] + o, vbuf + pc_base[1][mt & 1] + o);
-  };
-  auto mix_mfma = [&](MixOps& m, int g, int nt) {
-    acc[g & 3][nt] = mfma32(m.av[g & 1], m.bp[nt], acc[g & 3][nt]);
-  };
-
   // Key-validity ballot of block j: bit k of the result = slot j * 32 + k
   // holds a row.
-  auto valid_mask = [&](int j) -> uint32_t {
+  auto valid_mask = [&](int j) __attribute__((always_inline)) -> uint32_t {
     const bool v_ok = row_of(j * kBlk + (lane & 31)) >= 0;
     return (uint32_t)__builtin_amdgcn_ballot_w64(v_ok);
   };
+  // x[v] is key 8 (v / 4) + 4 hh + v % 4 of the block.
+  auto key_ok = [&](uint32_t vmj, int v) __attribute__((always_inline)) -> bool {
+    return ((vmj >> (8 * (v >> 2) + 4 * hh + (v & 3))) & 1u) != 0;
+  };
+  // Raw scores of block j (scale applied, -inf where masked).
+  auto write_scores = [&](int j, const f32x16& x, uint32_t vmj) __attribute__((always_inline)) {
+    float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * kBlk;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (j * kBlk + kloc < nslot) so[kloc] = key_ok(vmj, v) ? x[v] * a.scale : -INFINITY;
+    }
+  };
+  // Before the softmax of a block: a block with masked keys is scaled here
+  // (-inf where masked) and its softmax factor becomes 1.
+  auto prepare = [&](f32x16& x, uint32_t vmj) __attribute__((always_inline)) -> float {
+    if (vmj == 0xffffffffu) return a.scale_log2;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = key_ok(vmj, v) ? x[v] * a.scale_log2 : -INFINITY;
+    return 1.f;
+  };
 
-  // Scores of block j with the first half (k-step 0) of the mix of block
-  // j - 1: the 36 score MFMAs form one dependent chain, and the 16 mix MFMAs
-  // sit on its even slots, in the chain's latency shadow.  Every LDS operand
-  // is read three or more slots ahead.  The gather `gn` goes out one line
-  // every fourth slot: a burst of gathers from four waves backs up the CU's
-  // address unit and would stall the issuing wave's MFMAs.  On exit `m` holds
-  // the k-step 1 P fragments and the first k-step 1 A fragment.
-  auto scores_mix = [&](int j, f32x16& sacc, MixOps& m, const Gather& gn) {
+  // Softmax of the block in x (this lane's 16 scores; cx takes them to log2
+  // units), in steps 0 .. kSoftSteps - 1 so that they can ride in the score
+  // chain's slots.  Leaves P in pb, the factor alpha for the accumulators and
+  // the wave-uniform decision resc_any to apply it.  Each step's results are
+  // pinned where they are computed; otherwise the compiler sinks the vector
+  // work below the chain to its uses in the mix.
+  float mloc = 0.f, mblk = 0.f, alpha = 1.f, mref = 0.f, lsum = 0.f;
+  bool resc_any = false;
+  auto soft_step = [&](int k, f32x16& x, float cx, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
+    if (k < 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * k + e] *= cx;
+      const float m4 = fmaxf(fmaxf(x[4 * k], x[4 * k + 1]), fmaxf(x[4 * k + 2], x[4 * k + 3]));
+      mloc = (k == 0) ? m4 : fmaxf(mloc, m4);
+      asm volatile("" : "+v"(mloc));
+    } else if (k == 4) {  // the other half of this head's keys sits in lane l ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+      mblk = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      asm volatile("" : "+v"(mblk));
+    } else if (k == 5) {
+      // Move the reference max when this block exceeds it by more than 2^8;
+      // a head's accumulators are still zero while its max is -inf.
+      const bool need = mblk > m_run + kRescaleLog2;
+      const bool resc = need && m_run != -INFINITY;
+      const float mnew = need ? mblk : m_run;
+      alpha = resc ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+      l_run *= alpha;
+      m_run = mnew;
+      mref = (m_run == -INFINITY) ? 0.f : m_run;
+      resc_any = __builtin_amdgcn_ballot_w64(resc) != 0;
+      asm volatile("" : "+v"(alpha), "+v"(l_run), "+v"(m_run), "+v"(mref));
+    } else if (k < 14) {
+      const int v = 2 * (k - 6);
+      x[v] = __builtin_amdgcn_exp2f(x[v] - mref);
+      x[v + 1] = __builtin_amdgcn_exp2f(x[v + 1] - mref);
+      const float s2 = x[v] + x[v + 1];
+      lsum = (k == 6) ? s2 : lsum + s2;
+      asm volatile("" : "+v"(x[v]), "+v"(x[v + 1]), "+v"(lsum));
+    } else if (k < 16) {
+      const int ks = k - 14;
+      const uint4 w = {pack2(x[8 * ks], x[8 * ks + 1]), pack2(x[8 * ks + 2], x[8 * ks + 3]),
+                       pack2(x[8 * ks + 4], x[8 * ks + 5]), pack2(x[8 * ks + 6], x[8 * ks + 7])};
+      pb[ks] = __builtin_bit_cast(bf16x8, w);
+      asm volatile("" : "+v"(pb[ks]));
+    } else {
+      l_run += lsum;
+      asm volatile("" : "+v"(l_run));
+    }
+  };
+
+  // Score chain of block j into sacc.  With SOFT, the softmax steps of the
+  // previous block (x) sit one per slot after the chain's first MFMA.  The
+  // gather `gn` goes out one line every fourth slot: a burst of gathers from
+  // four waves backs up the CU's address unit and would stall the chain.
+  // Every score operand is read three slots ahead.
+  auto chain = [&](auto soft_tag, int j, f32x16& sacc, f32x16& x, float cx, bf16x8 (&pb)[2], const Gather& gn) __attribute__((always_inline)) {
+    constexpr bool SOFT = decltype(soft_tag)::value;
     const char LDS_AS* kbuf = s3 + (j % kNbuf) * kBufBytes;
-    const int p = j - 1;
     constexpr int AH = 3;
     bf16x8 ring[AH + 1];
     auto qk_ld = [&](int st) {
@@ -771,200 +792,128 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     };
 #pragma unroll
     for (int st = 0; st < AH; ++st) ring[st] = qk_ld(st);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) m.bp[nt] = bp_ld(p, 0, nt);
-    m.av[0] = av_ld(p, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
-      if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
-      // Mix MFMA i = 4 g + nt (g = 0..3) runs in slot 2 i; A of group g + 1
-      // loads when group g starts, k-step 1's P once k-step 0's is used up.
-      if ((k & 7) == 0 && k < 32) m.av[((k >> 3) + 1) & 1] = av_ld(p, (k >> 3) + 1);
-      if (k >= 32) m.bp[k - 32] = bp_ld(p, 1, k - 32);
       if ((k & 3) == 0) gather_line(gn, k >> 2);
+      if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
       else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
       else mfma32_v(sacc, kf, qf[k]);
-      if ((k & 1) == 0 && k < 32) mix_mfma(m, k >> 3, (k >> 1) & 3);
+      if (SOFT && k >= 1 && k <= kSoftSteps) soft_step(k - 1, x, cx, pb);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Softmax of block j (this lane: head `head`, 16 keys), then publish P(j)
-  // and the rescale factors of this wave's heads.  With MIX, the second half
-  // (k-step 1, groups 4..7) of the mix of block j - 1 is spread over its
-  // stages, so the matrix pipe runs under the softmax's vector work.
-  auto softmax = [&](auto mix_tag, int j, const f32x16& sacc, uint32_t vm, MixOps& m) {
-    constexpr bool MIX = decltype(mix_tag)::value;
-    const int p = j - 1;
-    auto mix_group = [&](int g) {
-      if constexpr (MIX) {
-        if (g < 7) m.av[(g + 1) & 1] = av_ld(p, g + 1);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) mix_mfma(m, g, nt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    const uint32_t vmh = vm >> (4 * hh);  // bit 8 (v / 4) + v % 4: key of sacc[v]
-    float t[16];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      t[v] = ((vmh >> (8 * (v >> 2) + (v & 3))) & 1u) ? sacc[v] * a.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, t[v]);
-    }
-    mix_group(4);
-    if (a.flags & 2u) {
-      float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * kBlk;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (j * kBlk + kloc < nslot) so[kloc] = ((vmh >> (8 * (v >> 2) + (v & 3))) & 1u) ? sacc[v] * a.scale : -INFINITY;
-      }
-    }
-    const float mblk = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // Move the reference max when this block exceeds it by more than 2^8; a
-    // head's accumulators are still zero while its max is -inf.
-    const bool need = mblk > m_run + kRescaleLog2;
-    const bool resc = need && m_run != -INFINITY;
-    const float mnew = need ? mblk : m_run;
-    const float alpha = resc ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-    l_run *= alpha;
-    m_run = mnew;
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-    mix_group(5);
-    float lsum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      t[v] = __builtin_amdgcn_exp2f(t[v] - mref);
-      lsum += t[v];
-    }
-    mix_group(6);
-#pragma unroll
-    for (int v = 8; v < 16; ++v) {
-      t[v] = __builtin_amdgcn_exp2f(t[v] - mref);
-      lsum += t[v];
-    }
-    l_run += lsum;
-    mix_group(7);
-    // Every wave must be done mixing block j - 1 (reading the P tile, the
-    // rescale flags and factors) before they are overwritten.
-    char* pw = smem + (j & 1) * kPBytes + pw_base;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint2*>(pw + 16 * q) = pack4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
-    const bool any = __builtin_amdgcn_ballot_w64(resc) != 0;
-    if (any && hh == 0) reinterpret_cast<float*>(smem + kOffAlpha)[kHeads * (j & 1) + head] = alpha;
-    if (lane == 0) flags[4 * (j & 1) + wave] = any ? 1 : 0;
-  };
-
-  // Wait for the gather of block j (the only memory instructions in flight)
-  // and for every wave to finish the previous iteration.
-  auto sync_block = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
+  // Blocks 0 and 1 go out now; the query loads resolve here with them (the
+  // operands then count as asm-defined, so no per-use vmcnt wait, which
+  // would also drain the in-order gathers, lands in the key loop).
   issue(0);
-  // Resolve the query loads here, while the first gather is in flight: the
-  // operands then count as asm-defined, so no per-use vmcnt wait (which would
-  // also drain the in-order gathers) lands in the key loop.
+  issue(1);
 #pragma unroll
   for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
-  sync_block();
-  issue(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  f32x16 prev;
+  uint32_t vm_prev = valid_mask(0);
   {
-    f32x16 sacc = {};
-    MixOps m;
-    const uint32_t vm = valid_mask(0);
-    scores(0, sacc);
-    softmax(std::false_type{}, 0, sacc, vm, m);
+    bf16x8 pb_unused[2];
+    f32x16 x_unused;
+    chain(std::false_type{}, 0, prev, x_unused, 1.f, pb_unused, gather_setup(2));
   }
   for (int j = 1; j < nblk; ++j) {
     // Per-lane LDS bases are re-derived each iteration rather than kept as
     // dozens of hoisted base + offset sums occupying registers.
     asm volatile("" : "+v"(qk_base[0]), "+v"(qk_base[1]), "+v"(qk_base[2]), "+v"(qk_base[3]));
     asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
-    asm volatile("" : "+v"(pr_base), "+v"(pw_base));
-    sync_block();
-    const Gather gn = gather_setup(j + 1);  // into buffer (j - 2) % 3, mixed last iteration
-    apply_rescale((j - 1) & 1);
+    // Block j complete (block j + 1's 9 loads are the only ones behind it)
+    // and every wave done with iteration j - 1.
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    __syncthreads();
+    if (a.flags & 2u) write_scores(j - 1, prev, vm_prev);
+    const float cx = prepare(prev, vm_prev);
+    const Gather gn = gather_setup(j + 2);
     const uint32_t vm = valid_mask(j);
-    f32x16 sacc = {};
-    MixOps m;
-    scores_mix(j, sacc, m, gn);
-    softmax(std::true_type{}, j, sacc, vm, m);
-  }
-  sync_block();
-  apply_rescale((nblk - 1) & 1);
-  mix(nblk - 1);
-
-  // Per-head (max, sum): lanes l and l ^ 32 hold halves of the sum.
-  l_run += __shfl_xor(l_run, 32);
-  float* stat = reinterpret_cast<float*>(smem + kOffStat);
-  if (hh == 0) {
-    stat[head] = m_run;
-    stat[kHeads + head] = l_run;
-  }
-  __syncthreads();
-  float lh[4], mh[4];
+    f32x16 sacc;
+    bf16x8 pb[2];
+    chain(std::true_type{}, j, sacc, prev, cx, pb, gn);
+    if (resc_any) rescale(alpha);
+    mix(j - 1, pb);
+    // The loop-carried scores are a copy made by explicit moves into
+    // registers of their own: were the allocator free to merge the two, it
+    // could move the accumulator into the loop registers between two chain
+    // MFMAs, reading a sum still in flight.
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    mh[nt] = stat[32 * nt + (lane & 31)];
-    lh[nt] = stat[kHeads + 32 * nt + (lane & 31)];
-  }
-  // acc[mt][nt][v]: column 128 w + 32 mt + 8 (v / 4) + 4 hh + v % 4, head 32 nt + lane % 32.
-  // The tile goes through LDS (the row buffers are free now) so that the
-  // global writes are whole 1 KB rows: tile row h holds head h's 512 columns
-  // as 64 16-byte chunks, chunk c stored at position c ^ (h & 63).  With one
-  // split it is the normalised O~; with several, each split stores its
-  // unnormalised sum with (max, sum) and the merge applies 2^(m_s - M) / L.
-  uint16_t* dst = (a.S == 1) ? a.o_latent + (int64_t)b * kHeads * kLatent
-                             : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int hd = 32 * nt + (lane & 31);
-    char* trow = smem + hd * 1024 + 8 * hh;
-    if (a.S == 1) {
-      const float inv = 1.0f / lh[nt];  // an empty selection gives 0 * inf = NaN
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = 16 * wave + 4 * mt + q4;
-          *reinterpret_cast<uint2*>(trow + ((c ^ (hd & 63)) << 4)) =
-              pack4(acc[mt][nt][4 * q4] * inv, acc[mt][nt][4 * q4 + 1] * inv, acc[mt][nt][4 * q4 + 2] * inv,
-                    acc[mt][nt][4 * q4 + 3] * inv);
-        }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = 16 * wave + 4 * mt + q4;
-          *reinterpret_cast<uint2*>(trow + ((c ^ (hd & 63)) << 4)) =
-              pack4(acc[mt][nt][4 * q4], acc[mt][nt][4 * q4 + 1], acc[mt][nt][4 * q4 + 2], acc[mt][nt][4 * q4 + 3]);
-        }
+    for (int v = 0; v < 16; ++v) {
+      float t;
+      asm volatile("v_mov_b32 %0, %1" : "=&v"(t) : "v"(sacc[v]));
+      prev[v] = t;
     }
-    if (wave == 0 && hh == 0) {
-      if (a.S == 1) {
+    vm_prev = vm;
+  }
+  {
+    if (a.flags & 2u) write_scores(nblk - 1, prev, vm_prev);
+    const float cx = prepare(prev, vm_prev);
+    bf16x8 pb[2];
+#pragma unroll
+    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, prev, cx, pb);
+    if (resc_any) rescale(alpha);
+    mix(nblk - 1, pb);
+  }
+
+  // This lane's head: lanes l and l ^ 32 hold halves of the sum.
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  // The masked gathers past the last block may still be landing; after
+  // this barrier the row buffers are free for the output tile.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // The wave's 32 heads go through LDS (tile row h = head h's 512 columns as
+  // 64 16-byte chunks, chunk c at position c ^ (h & 63), the two 8-byte
+  // halves swapped when bit 4 of h is set) so that the global writes are
+  // whole 1 KB rows.  With one split it is the normalised O~; with several,
+  // each split stores its unnormalised sum with (max, sum) and the merge
+  // applies 2^(m_s - M) / L.  One column tile at a time: the scheduling
+  // barriers keep the accumulators from being read all at once.
+  {
+    const uint32_t half = 8u * (uint32_t)(hh ^ ((head >> 4) & 1));
+    char* trow = smem + head * 1024 + half;
+    const float inv = SPLIT ? 1.f : 1.0f / l_run;  // an empty selection gives 0 * inf = NaN
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = SPLIT ? acc[mt][4 * q4 + e] : acc[mt][4 * q4 + e] * inv;
+        *reinterpret_cast<uint2*>(trow + (((4 * mt + q4) ^ (head & 63)) << 4)) = pack4(o[0], o[1], o[2], o[3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (hh == 0) {
+      if constexpr (!SPLIT) {
         if (a.lse != nullptr)
-          a.lse[(int64_t)b * kHeads + hd] = lh[nt] > 0.f ? (mh[nt] + __log2f(lh[nt])) * kLn2 : -INFINITY;
-        if (validate && hd == 0 && !(lh[nt] > 0.f)) atomicOr(a.status, 4u);
+          a.lse[(int64_t)b * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        if (validate && !(l_run > 0.f)) atomicOr(a.status, 4u);
       } else {
-        float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + hd) * 2;
-        pml[0] = mh[nt];
-        pml[1] = lh[nt];
+        float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + head) * 2;
+        pml[0] = m_run;
+        pml[1] = l_run;
       }
     }
   }
-  __syncthreads();
-  // Wave w copies rows w, w + 4, ...: lane l moves chunk l of the row.
-#pragma unroll 4
-  for (int h = wave; h < kHeads; h += 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(smem + h * 1024 + ((lane ^ (h & 63)) << 4));
+  // Row r of the wave's tile: lane l moves chunk l (the tile is the wave's
+  // own, so no barrier: LDS operations of one wave complete in order).
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) {
+    const int h = 32 * wave + r;
+    uint4 v = *reinterpret_cast<const uint4*>(smem + h * 1024 + ((lane ^ (h & 63)) << 4));
+    if (r & 16) v = uint4{v.z, v.w, v.x, v.y};
     *reinterpret_cast<uint4*>(dst + (int64_t)h * kLatent + 8 * lane) = v;
   }
 }
@@ -1065,10 +1014,9 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
   const int units = a.B * a.S;
   const int grid = 8 * ((units + 7) / 8);  // whole XCD rounds; spare workgroups exit
-  if (a.indices == nullptr)
-    hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(256), 0, st, a);
+  auto* k = a.indices == nullptr ? (a.S > 1 ? decode_kernel<true, true> : decode_kernel<true, false>)
+                                  : (a.S > 1 ? decode_kernel<false, true> : decode_kernel<false, false>);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
