@@ -469,10 +469,11 @@ constexpr int kNbuf = 4;                    // row buffers
 constexpr int kBufBytes = 72 * kBlk * 16;   // 36864: one block of rows
 constexpr int kOffIdx = kNbuf * kBufBytes;  // int [kIdxCap]
 constexpr int kDecodeLds = kOffIdx + kIdxCap * 4;
-constexpr int kSoftSteps = 17;              // softmax steps placed in the score chain
+constexpr int kSoftSteps = 32;              // softmax steps placed beside MFMAs
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
-static_assert(kHeads * 1024 <= kOffIdx, "the epilogue tile must stay inside the row buffers");
-static_assert(kSoftSteps < 36, "the softmax steps must fit the score chain");
+constexpr int kTilePitch = 1040;            // output tile row: 512 bf16 + 16 bytes of padding
+static_assert(kHeads * kTilePitch <= kOffIdx, "the epilogue tile must stay inside the row buffers");
+static_assert(kSoftSteps <= 32, "the softmax steps must fit the score chain and the mix");
 
 template <bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
@@ -678,27 +679,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     asm volatile("s_nop 3" ::: "memory");
   };
 
-  // Mix of block p (rows in buffer p % 4) with this wave's P fragments pb[ks]:
-  // fragment i = 16 ks + mt, one MFMA each, A fragments read four ahead.
-  auto mix = [&](int p, const bf16x8 (&pb)[2]) __attribute__((always_inline)) {
-    const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
-    auto av_ld = [&](int i) {
-      const int ks = i >> 4, mt = i & 15;
-      const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
-      return tr_pair(buf + pc_base[0][mt & 1] + o, buf + pc_base[1][mt & 1] + o);
-    };
-    constexpr int MA = 4;
-    bf16x8 ring[MA + 1];
-#pragma unroll
-    for (int i = 0; i < MA; ++i) ring[i] = av_ld(i);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i + MA < 32) ring[(i + MA) % (MA + 1)] = av_ld(i + MA);
-      acc[i & 15] = mfma32(ring[i % (MA + 1)], pb[i >> 4], acc[i & 15]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
   // Key-validity ballot of block j: bit k of the result = slot j * 32 + k
   // holds a row.
   auto valid_mask = [&](int j) __attribute__((always_inline)) -> uint32_t {
@@ -728,52 +708,80 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   };
 
   // Softmax of the block in x (this lane's 16 scores; cx takes them to log2
-  // units), in steps 0 .. kSoftSteps - 1 so that they can ride in the score
-  // chain's slots.  Leaves P in pb, the factor alpha for the accumulators and
-  // the wave-uniform decision resc_any to apply it.  Each step's results are
-  // pinned where they are computed; otherwise the compiler sinks the vector
-  // work below the chain to its uses in the mix.
+  // units), in steps 0 .. kSoftSteps - 1 of a few vector instructions each,
+  // so that each fits the issue slot beside one MFMA.  Leaves P in pb, the
+  // factor alpha for the accumulators and the wave-uniform decision resc_any
+  // to apply it.  Each step's results are pinned where they are computed;
+  // otherwise the compiler sinks the vector work to its uses in the mix.
   float mloc = 0.f, mblk = 0.f, alpha = 1.f, mref = 0.f, lsum = 0.f;
-  bool resc_any = false;
+  bool resc = false, resc_any = false;
+  uint32_t pk[8];  // P as bf16 pairs, keys in the order of x
   auto soft_step = [&](int k, f32x16& x, float cx, bf16x8 (&pb)[2]) __attribute__((always_inline)) {
-    if (k < 4) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * k + e] *= cx;
-      const float m4 = fmaxf(fmaxf(x[4 * k], x[4 * k + 1]), fmaxf(x[4 * k + 2], x[4 * k + 3]));
-      mloc = (k == 0) ? m4 : fmaxf(mloc, m4);
-      asm volatile("" : "+v"(mloc));
-    } else if (k == 4) {  // the other half of this head's keys sits in lane l ^ 32
+    if (k < 8) {  // scale two scores, running max
+      x[2 * k] *= cx;
+      x[2 * k + 1] *= cx;
+      const float m2 = fmaxf(x[2 * k], x[2 * k + 1]);
+      mloc = (k == 0) ? m2 : fmaxf(mloc, m2);
+      asm volatile("" : "+v"(x[2 * k]), "+v"(x[2 * k + 1]), "+v"(mloc));
+    } else if (k == 8) {  // the other half of this head's keys sits in lane l ^ 32
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
       mblk = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       asm volatile("" : "+v"(mblk));
-    } else if (k == 5) {
+    } else if (k == 9) {
       // Move the reference max when this block exceeds it by more than 2^8;
       // a head's accumulators are still zero while its max is -inf.
       const bool need = mblk > m_run + kRescaleLog2;
-      const bool resc = need && m_run != -INFINITY;
+      resc = need && m_run != -INFINITY;
       const float mnew = need ? mblk : m_run;
       alpha = resc ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
-      l_run *= alpha;
+      mref = (mnew == -INFINITY) ? 0.f : mnew;
       m_run = mnew;
-      mref = (m_run == -INFINITY) ? 0.f : m_run;
+      asm volatile("" : "+v"(alpha), "+v"(m_run), "+v"(mref));
+    } else if (k == 10) {
+      l_run *= alpha;
       resc_any = __builtin_amdgcn_ballot_w64(resc) != 0;
-      asm volatile("" : "+v"(alpha), "+v"(l_run), "+v"(m_run), "+v"(mref));
-    } else if (k < 14) {
-      const int v = 2 * (k - 6);
+      asm volatile("" : "+v"(l_run));
+    } else if (k < 27) {  // one probability per step
+      const int v = k - 11;
       x[v] = __builtin_amdgcn_exp2f(x[v] - mref);
-      x[v + 1] = __builtin_amdgcn_exp2f(x[v + 1] - mref);
-      const float s2 = x[v] + x[v + 1];
-      lsum = (k == 6) ? s2 : lsum + s2;
-      asm volatile("" : "+v"(x[v]), "+v"(x[v + 1]), "+v"(lsum));
-    } else if (k < 16) {
-      const int ks = k - 14;
-      const uint4 w = {pack2(x[8 * ks], x[8 * ks + 1]), pack2(x[8 * ks + 2], x[8 * ks + 3]),
-                       pack2(x[8 * ks + 4], x[8 * ks + 5]), pack2(x[8 * ks + 6], x[8 * ks + 7])};
-      pb[ks] = __builtin_bit_cast(bf16x8, w);
-      asm volatile("" : "+v"(pb[ks]));
+      lsum = (v == 0) ? x[v] : lsum + x[v];
+      asm volatile("" : "+v"(x[v]), "+v"(lsum));
+    } else if (k < 31) {  // pack P, four probabilities per step
+      const int q = 2 * (k - 27);
+      pk[q] = pack2(x[2 * q], x[2 * q + 1]);
+      pk[q + 1] = pack2(x[2 * q + 2], x[2 * q + 3]);
+      asm volatile("" : "+v"(pk[q]), "+v"(pk[q + 1]));
     } else {
+      pb[0] = __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+      pb[1] = __builtin_bit_cast(bf16x8, uint4{pk[4], pk[5], pk[6], pk[7]});
       l_run += lsum;
       asm volatile("" : "+v"(l_run));
+    }
+  };
+
+  // Mix of block p (rows in buffer p % 4) with this wave's P fragments pb[ks]:
+  // fragment i = 16 ks + mt, one MFMA each, A fragments read four ahead.
+  // With SOFT, the softmax steps of the next block (x -> pn) ride beside the
+  // MFMAs, one per MFMA.
+  auto mix = [&](auto soft_tag, int p, const bf16x8 (&pb)[2], f32x16& x, float cx,
+                 bf16x8 (&pn)[2]) __attribute__((always_inline)) {
+    constexpr bool SOFT = decltype(soft_tag)::value;
+    const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
+    auto av_ld = [&](int i) {
+      const int ks = i >> 4, mt = i & 15;
+      const uint32_t o = (uint32_t)((mt >> 1) * kBlk * 128 + ks * 16 * 128);
+      return tr_pair(buf + pc_base[0][mt & 1] + o, buf + pc_base[1][mt & 1] + o);
+    };
+    constexpr int MA = 4;
+    bf16x8 ring[MA + 1];
+#pragma unroll
+    for (int i = 0; i < MA; ++i) ring[i] = av_ld(i);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + MA < 32) ring[(i + MA) % (MA + 1)] = av_ld(i + MA);
+      acc[i & 15] = mfma32(ring[i % (MA + 1)], pb[i >> 4], acc[i & 15]);
+      if (SOFT && i < kSoftSteps) soft_step(i, x, cx, pn);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -816,22 +824,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  f32x16 prev;
+  f32x16 prev, x_unused;
+  bf16x8 pb_unused[2], pb_last[2];
   uint32_t vm_prev = valid_mask(0);
-  {
-    bf16x8 pb_unused[2];
-    f32x16 x_unused;
-    chain(std::false_type{}, 0, prev, x_unused, 1.f, pb_unused, gather_setup(2));
-  }
-  for (int j = 1; j < nblk; ++j) {
+  chain(std::false_type{}, 0, prev, x_unused, 1.f, pb_unused, gather_setup(2));
+  // Top of iteration j: block j complete (block j + 1's 9 loads are the only
+  // ones behind it) and every wave done with iteration j - 1.
+  auto block_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    __syncthreads();
+  };
+  int j = 1;
+  for (; j + 1 < nblk; ++j) {
     // Per-lane LDS bases are re-derived each iteration rather than kept as
     // dozens of hoisted base + offset sums occupying registers.
     asm volatile("" : "+v"(qk_base[0]), "+v"(qk_base[1]), "+v"(qk_base[2]), "+v"(qk_base[3]));
     asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
-    // Block j complete (block j + 1's 9 loads are the only ones behind it)
-    // and every wave done with iteration j - 1.
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    __syncthreads();
+    block_barrier();
     if (a.flags & 2u) write_scores(j - 1, prev, vm_prev);
     const float cx = prepare(prev, vm_prev);
     const Gather gn = gather_setup(j + 2);
@@ -840,7 +849,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     bf16x8 pb[2];
     chain(std::true_type{}, j, sacc, prev, cx, pb, gn);
     if (resc_any) rescale(alpha);
-    mix(j - 1, pb);
+    mix(std::false_type{}, j - 1, pb, x_unused, 1.f, pb_unused);
     // The loop-carried scores are a copy made by explicit moves into
     // registers of their own: were the allocator free to merge the two, it
     // could move the accumulator into the loop registers between two chain
@@ -853,15 +862,28 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     }
     vm_prev = vm;
   }
-  {
-    if (a.flags & 2u) write_scores(nblk - 1, prev, vm_prev);
+  if (nblk > 1) {
+    // The last iteration, peeled: the softmax of the last block rides beside
+    // the mix of the one before.
+    block_barrier();
+    if (a.flags & 2u) write_scores(j - 1, prev, vm_prev);
     const float cx = prepare(prev, vm_prev);
+    const uint32_t vm = valid_mask(j);
+    f32x16 sacc;
     bf16x8 pb[2];
-#pragma unroll
-    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, prev, cx, pb);
+    chain(std::true_type{}, j, sacc, prev, cx, pb, gather_setup(j + 2));
     if (resc_any) rescale(alpha);
-    mix(nblk - 1, pb);
+    if (a.flags & 2u) write_scores(j, sacc, vm);
+    const float cl = prepare(sacc, vm);
+    mix(std::true_type{}, j - 1, pb, sacc, cl, pb_last);
+  } else {
+    if (a.flags & 2u) write_scores(0, prev, vm_prev);
+    const float cx = prepare(prev, vm_prev);
+#pragma unroll
+    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, prev, cx, pb_last);
   }
+  if (resc_any) rescale(alpha);
+  mix(std::false_type{}, nblk - 1, pb_last, x_unused, 1.f, pb_unused);
 
   // This lane's head: lanes l and l ^ 32 hold halves of the sum.
   {
@@ -873,16 +895,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // The wave's 32 heads go through LDS (tile row h = head h's 512 columns as
-  // 64 16-byte chunks, chunk c at position c ^ (h & 63), the two 8-byte
-  // halves swapped when bit 4 of h is set) so that the global writes are
-  // whole 1 KB rows.  With one split it is the normalised O~; with several,
+  // The wave's 32 heads go through LDS (tile row h = head h's 512 columns at
+  // h * kTilePitch, the two 8-byte halves of each 16-byte chunk swapped when
+  // bit 4 of h is set; with the padded pitch, the 32 heads of one store hit
+  // distinct banks) so that the global writes are whole 1 KB rows.  With one split it is the normalised O~; with several,
   // each split stores its unnormalised sum with (max, sum) and the merge
   // applies 2^(m_s - M) / L.  One column tile at a time: the scheduling
   // barriers keep the accumulators from being read all at once.
   {
     const uint32_t half = 8u * (uint32_t)(hh ^ ((head >> 4) & 1));
-    char* trow = smem + head * 1024 + half;
+    char* trow = smem + head * kTilePitch + half;
     const float inv = SPLIT ? 1.f : 1.0f / l_run;  // an empty selection gives 0 * inf = NaN
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
@@ -891,7 +913,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
         float o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = SPLIT ? acc[mt][4 * q4 + e] : acc[mt][4 * q4 + e] * inv;
-        *reinterpret_cast<uint2*>(trow + (((4 * mt + q4) ^ (head & 63)) << 4)) = pack4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint2*>(trow + 16 * (4 * mt + q4)) = pack4(o[0], o[1], o[2], o[3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -912,7 +934,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 #pragma unroll 8
   for (int r = 0; r < 32; ++r) {
     const int h = 32 * wave + r;
-    uint4 v = *reinterpret_cast<const uint4*>(smem + h * 1024 + ((lane ^ (h & 63)) << 4));
+    uint4 v = *reinterpret_cast<const uint4*>(smem + h * kTilePitch + 16 * lane);
     if (r & 16) v = uint4{v.z, v.w, v.x, v.y};
     *reinterpret_cast<uint4*>(dst + (int64_t)h * kLatent + 8 * lane) = v;
   }

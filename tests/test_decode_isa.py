@@ -79,9 +79,9 @@ def decode_asm():
 
 def test_score_chains_untouched(decode_asm):
     chains, problems = chain_violations(decode_asm)
-    # 4 kernels (dense/sparse x one split/several), each with the first
-    # block's chain and the loop's chain.
-    assert chains == 8
+    # 4 kernels (dense/sparse x one split/several), each with at least the
+    # first block's chain and the loop's chain.
+    assert chains >= 8
     assert not problems, "\n".join(problems[:10])
 
 
