@@ -271,6 +271,7 @@ constexpr int kVuSplits = 4;  // splits staged per pass
 template <bool FUSED, int ROWS>
 __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   __shared__ __attribute__((aligned(1024))) char slots[kVuSplits * ROWS * kOtRow];
+  __shared__ float wtab[ROWS * 64];  // merge weights: per wave, row, split
   constexpr int RPW = ROWS / 4;  // batch rows per wave
   const int ntiles = (a.B + ROWS - 1) / ROWS;
   const int units = kHeads * ntiles;
@@ -282,11 +283,6 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nrows = min(ROWS, a.B - b0);  // valid rows of the tile
   const int r0 = RPW * wave;              // first tile row of this wave
-
-  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
-  bf16x8 wf[32];
-#pragma unroll
-  for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
 
   const int S = FUSED ? a.S : 1;
   const int64_t sstride = (int64_t)a.B * kHeads;  // rows per split
@@ -308,70 +304,68 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
               (uint32_t)j * kHeads * kLatent * 2u + 16u * (uint32_t)lane);
     }
   };
+  // Issue order: this wave's first partial rows, its splits' (max, sum), then
+  // W_UV,h.  vmcnt retires in order, so the merge weights and the merge can
+  // start once the first two have landed while W_UV,h is still on its way
+  // (at least 32 loads of it follow; the waits below count on that).
+  gather(0);
 
-  // Merge weights: lane s loads split s's (max, sum) of each of the wave's
-  // rows before the first gather goes out; once everything has landed (one
-  // round trip) every lane reads them back with readlane and computes the
-  // same M and L, so no memory access or cross-lane exchange sits between the
-  // data and the merge.  S <= 64.
-  float v[RPW][8];
-  float Mx[RPW], iL[RPW];
-  float2 mlv[RPW];
+  // (max, sum) loads, lane-parallel: in pass q lane l takes row
+  // j = q R + l / G and split s = l % G, with G = S rounded up to a power of
+  // two and R = 64 / G rows per pass.
+  const int G = S <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(S - 1)));
+  const int gsh = __builtin_ctz((unsigned)G);
+  const int R = 64 >> gsh;
+  constexpr int kMaxPasses = RPW;  // G = 64
+  float2 mlv[kMaxPasses];
   if constexpr (FUSED) {
-    const int ls = min(lane, S - 1);
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int64_t bh = (int64_t)min(b0 + r0 + j, a.B - 1) * kHeads + h;
-      mlv[j] = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)ls * sstride + bh) * 2);
+    for (int q = 0; q < kMaxPasses; ++q) {
+      mlv[q] = float2{-INFINITY, 0.f};
+      if (q * R >= RPW) continue;
+      const int j = q * R + (lane >> gsh), sp = lane & (G - 1);
+      if (j < RPW && sp < S) {
+        const int64_t bh = (int64_t)min(b0 + r0 + j, a.B - 1) * kHeads + h;
+        mlv[q] = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)sp * sstride + bh) * 2);
+      }
     }
   }
-  gather(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  auto lane_f = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+
+  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
+  bf16x8 wf[32];
+#pragma unroll
+  for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
+
+  // Merge weights g_s = 2^(m_s - M) / L of the row, from a group max and a
+  // group sum over the row's G lanes, into a per-wave table (an all -inf row
+  // gets NaN weights: an empty selection, as in mla_combine).
+  float* wt = reinterpret_cast<float*>(wtab) + wave * RPW * 64;
   if constexpr (FUSED) {
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      float M = -INFINITY, L = 0.f;
-      if (S <= kVuSplits) {
-        // Straight-line form for the usual split counts: the rows' chains
-        // are independent (a runtime loop serialises readlane -> VALU).
-        float m[kVuSplits], l[kVuSplits];
-#pragma unroll
-        for (int sp = 0; sp < kVuSplits; ++sp) {
-          m[sp] = sp < S ? lane_f(mlv[j].x, sp) : -INFINITY;
-          l[sp] = lane_f(mlv[j].y, sp);
-          M = fmaxf(M, m[sp]);
-        }
-#pragma unroll
-        for (int sp = 0; sp < kVuSplits; ++sp)
-          L += (m[sp] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[sp] - M) * l[sp];
-      } else {
-        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, lane_f(mlv[j].x, sp));
-        for (int sp = 0; sp < S; ++sp) {
-          const float m = lane_f(mlv[j].x, sp);
-          L += (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M) * lane_f(mlv[j].y, sp);
-        }
-      }
-      Mx[j] = M;
-      iL[j] = 1.0f / L;
-      const float empty = L > 0.f ? 0.f : __builtin_nanf("");  // all -inf row: NaN, as in mla_combine
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[j][k] = empty;
-      if (lane == 0 && r0 + j < nrows) {
+    for (int q = 0; q < kMaxPasses; ++q) {
+      if (q * R >= RPW) continue;
+      const int j = q * R + (lane >> gsh), sp = lane & (G - 1);
+      float M = mlv[q].x;
+      for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+      const float e = (mlv[q].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mlv[q].x - M);
+      float L = e * mlv[q].y;
+      for (int o = 1; o < G; o <<= 1) L += __shfl_xor(L, o);
+      if (j < RPW && sp < S) wt[j * 64 + sp] = L > 0.f ? e / L : __builtin_nanf("");
+      if (j < RPW && sp == 0 && r0 + j < nrows) {
         const int64_t bh = (int64_t)(b0 + r0 + j) * kHeads + h;
         if (a.lse != nullptr) a.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         if (a.status != nullptr && h == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
       }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      Mx[j] = 0.f;
-      iL[j] = 1.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[j][k] = 0.f;
-    }
   }
+  float v[RPW][8];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[j][k] = 0.f;
+  // The first partial rows have landed once at most the 32 W_UV loads are
+  // outstanding.
+  asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
 
   for (int c0 = 0; c0 < S; c0 += kVuSplits) {
     if (c0 > 0) {
@@ -387,11 +381,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
       if (sc >= nc) break;
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
-        float gs = 1.f;
-        if constexpr (FUSED) {
-          const float m = lane_f(mlv[j].x, c0 + sc);
-          gs = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mx[j]) * iL[j];
-        }
+        const float gs = FUSED ? wt[j * 64 + c0 + sc] : 1.f;
         const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + (sc * ROWS + r0 + j) * kOtRow + 16 * lane);
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[k];
