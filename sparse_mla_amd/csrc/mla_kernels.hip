@@ -97,13 +97,17 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // of its MFMAs (such a copy would read a sum still in flight).  Wait states
 // after every MFMA would rule that out, but they stall the wave's issue
 // behind the matrix pipe and roughly double the chain's time.
+// mfma32_v also takes the previous chain MFMA's A operand (`keep`, unused):
+// that register then stays allocated until this dependent MFMA issues, so
+// the compiler puts no vector result in it while the matrix core may still
+// be reading it (the write would wait for the read to finish).
 __device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
   f32x16 c;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
   return c;
 }
-__device__ __forceinline__ void mfma32_v(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+__device__ __forceinline__ void mfma32_v(f32x16& c, bf16x8 a, bf16x8 b, bf16x8 keep) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b), "v"(keep));
 }
 __device__ __forceinline__ void mfma32_v_last(f32x16& c, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
@@ -779,7 +783,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // previous block (x) sit one per slot after the chain's first MFMA.  The
   // gather `gn` goes out one line every fourth slot: a burst of gathers from
   // four waves backs up the CU's address unit and would stall the chain.
-  // Every score operand is read three slots ahead.
+  // Every score operand is read three slots ahead; a ring slot is reloaded
+  // after the MFMA that follows its last use has issued.
   auto chain = [&](auto soft_tag, int j, f32x16& sacc, f32x16& x, float cx, bf16x8 (&pb)[2], const Gather& gn) __attribute__((always_inline)) {
     constexpr bool SOFT = decltype(soft_tag)::value;
     const char LDS_AS* kbuf = s3 + (j % kNbuf) * kBufBytes;
@@ -794,11 +799,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
       if ((k & 3) == 0) gather_line(gn, k >> 2);
-      if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
       else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
-      else mfma32_v(sacc, kf, qf[k]);
+      else mfma32_v(sacc, kf, qf[k], ring[(k + AH) % (AH + 1)]);
+      if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
       if (SOFT && k >= 1 && k <= kSoftSteps) soft_step(k - 1, x, cx, pb);
       __builtin_amdgcn_sched_barrier(0);
     }
