@@ -40,7 +40,7 @@ struct DecodeArgs {
   int32_t S;                // splits
   float scale;              // softmax scale
   float scale_log2;         // softmax scale * log2(e)
-  uint16_t* part_o;         // [S][B][128][512] bf16, normalised per split (S > 1)
+  uint16_t* part_o;         // [S][B][128][512] bf16, unnormalised sum per split (S > 1)
   float* part_ml;           // [S][B][128][2]   (max, sum) per split      (S > 1)
   uint16_t* o_latent;       // [B][128][512]    when S == 1
   float* lse;               // [B][128]         when S == 1 (may be NULL)
