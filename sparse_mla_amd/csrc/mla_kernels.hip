@@ -277,6 +277,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   __shared__ __attribute__((aligned(1024))) char slots[kVuSplits * ROWS * kOtRow];
   __shared__ float wtab[ROWS * 64];  // merge weights: per wave, row, split
   constexpr int RPW = ROWS / 4;  // batch rows per wave
+  static_assert(32 % (kVuSplits * RPW) == 0, "W_UV loads spread evenly over the first merge pass");
   const int ntiles = (a.B + ROWS - 1) / ROWS;
   const int units = kHeads * ntiles;
   const int per_xcd = (units + 7) >> 3;
@@ -308,10 +309,10 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
               (uint32_t)j * kHeads * kLatent * 2u + 16u * (uint32_t)lane);
     }
   };
-  // Issue order: this wave's first partial rows, its splits' (max, sum), then
-  // W_UV,h.  vmcnt retires in order, so the merge weights and the merge can
-  // start once the first two have landed while W_UV,h is still on its way
-  // (at least 32 loads of it follow; the waits below count on that).
+  // Order: this wave's first partial rows and its splits' (max, sum); once
+  // they have landed, W_UV,h, spread over the steps of the first merge pass
+  // (issued at once, the 32 loads per lane stall the wave's issue until most
+  // of them have returned, and the merge would wait behind them).
   gather(0);
 
   // (max, sum) loads, lane-parallel: in pass q lane l takes row
@@ -335,10 +336,10 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
     }
   }
 
+  // The partial rows (this wave's own LDS slots) and (max, sum) are in.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
   bf16x8 wf[32];
-#pragma unroll
-  for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
 
   // Merge weights g_s = 2^(m_s - M) / L of the row, from a group max and a
   // group sum over the row's G lanes, into a per-wave table (an all -inf row
@@ -367,29 +368,44 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   for (int j = 0; j < RPW; ++j)
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[j][k] = 0.f;
-  // The first partial rows have landed once at most the 32 W_UV loads are
-  // outstanding.
-  asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
 
-  for (int c0 = 0; c0 < S; c0 += kVuSplits) {
-    if (c0 > 0) {
-      // The previous pass's slot reads must be complete before its slots are
-      // gathered into again.
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      gather(c0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+  // Merge step (split sc of this pass, row j).
+  auto merge_step = [&](int c0, int sc, int j) __attribute__((always_inline)) {
+    const float gs = FUSED ? wt[j * 64 + c0 + sc] : 1.f;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + (sc * ROWS + r0 + j) * kOtRow + 16 * lane);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[k];
+  };
+  // First pass: the W_UV,h loads ride beside the merge steps, 32 / (4 RPW)
+  // per step; the steps of splits past S are skipped, their loads are not.
+  {
+    const int nc = min(kVuSplits, S);
+    constexpr int kLoadsPerStep = 32 / (kVuSplits * RPW);
+#pragma unroll
+    for (int sc = 0; sc < kVuSplits; ++sc)
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+#pragma unroll
+        for (int u = 0; u < kLoadsPerStep; ++u) {
+          const int st = (sc * RPW + j) * kLoadsPerStep + u;
+          wf[st] = ld8(w + 16 * st);
+        }
+        if (sc < nc) merge_step(0, sc, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  for (int c0 = kVuSplits; c0 < S; c0 += kVuSplits) {
+    // The previous pass's slot reads must be complete before its slots are
+    // gathered into again.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    gather(c0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int nc = min(kVuSplits, S - c0);
 #pragma unroll
     for (int sc = 0; sc < kVuSplits; ++sc) {
       if (sc >= nc) break;
 #pragma unroll
-      for (int j = 0; j < RPW; ++j) {
-        const float gs = FUSED ? wt[j * 64 + c0 + sc] : 1.f;
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + (sc * ROWS + r0 + j) * kOtRow + 16 * lane);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[k];
-      }
+      for (int j = 0; j < RPW; ++j) merge_step(c0, sc, j);
     }
   }
   // Merged rows (bf16) into the split-0 slots; every wave's rows must be
