@@ -292,20 +292,26 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   const int S = FUSED ? a.S : 1;
   const int64_t sstride = (int64_t)a.B * kHeads;  // rows per split
   const uint32_t lds0 = (uint32_t)(uintptr_t)(char LDS_AS*)slots;
-  const int wave_rows = min(RPW, max(0, nrows - r0));  // rows of this wave that exist
-  // Gather splits c0 .. c0 + 3 of the wave's rows: one instruction per
-  // (split, row); lane l brings bytes 16 l .. of the row.  The record size
-  // stops at the wave's last valid row (later rows read as zeros).
+  const int n = min(RPW, max(0, nrows - r0));  // rows of this wave that exist
+  // The wave's own LDS slots hold kCap rows; a pass stages splits
+  // c0 .. c0 + ps - 1 of its n rows, split c0 + c row j in slot q = c n + j
+  // (slot (q / RPW) ROWS + r0 + q % RPW of the array), so a wave with few
+  // rows takes more splits per pass.
+  constexpr int kCap = kVuSplits * RPW;
+  auto pass_splits = [&](int c0) { return min(S - c0, kCap / max(n, 1)); };
+  auto slot_of = [&](int q) { return (q / RPW) * ROWS + r0 + (q % RPW); };
+  // Gather one pass: one instruction per (split, row); lane l brings bytes
+  // 16 l .. of the row.
   auto gather = [&](int c0) {
-    const int nc = min(kVuSplits, S - c0);
-    for (int sc = 0; sc < nc; ++sc) {
-      const int64_t row0 = wave_rows > 0 ? (int64_t)(b0 + r0) * kHeads + h : 0;
-      const uint16_t* base = FUSED ? a.part_o + ((int64_t)(c0 + sc) * sstride + row0) * kLatent
+    if (n == 0) return;
+    const int ps = pass_splits(c0);
+    const int64_t row0 = (int64_t)(b0 + r0) * kHeads + h;
+    for (int c = 0; c < ps; ++c) {
+      const uint16_t* base = FUSED ? a.part_o + ((int64_t)(c0 + c) * sstride + row0) * kLatent
                                    : a.o_latent + row0 * kLatent;
-      const i32x4 rs = buffer_rsrc(base, wave_rows == 0 ? 0u : (uint32_t)(wave_rows - 1) * kHeads * kLatent * 2u + 1024u);
-#pragma unroll
-      for (int j = 0; j < RPW; ++j)
-        dma16(rs, lds0 + (uint32_t)((sc * ROWS + r0 + j) * kOtRow),
+      const i32x4 rs = buffer_rsrc(base, (uint32_t)(n - 1) * kHeads * kLatent * 2u + 1024u);
+      for (int j = 0; j < n; ++j)
+        dma16(rs, lds0 + (uint32_t)(slot_of(c * n + j) * kOtRow),
               (uint32_t)j * kHeads * kLatent * 2u + 16u * (uint32_t)lane);
     }
   };
@@ -369,16 +375,17 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[j][k] = 0.f;
 
-  // Merge step (split sc of this pass, row j).
-  auto merge_step = [&](int c0, int sc, int j) __attribute__((always_inline)) {
-    const float gs = FUSED ? wt[j * 64 + c0 + sc] : 1.f;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + (sc * ROWS + r0 + j) * kOtRow + 16 * lane);
+  // Merge step: split c0 + c of the pass, row j.
+  auto merge_step = [&](int c0, int c, int j) __attribute__((always_inline)) {
+    const float gs = FUSED ? wt[j * 64 + c0 + c] : 1.f;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(slots + slot_of(c * n + j) * kOtRow + 16 * lane);
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[k];
   };
-  // First pass: the W_UV,h loads ride beside the merge steps, 32 / (4 RPW)
-  // per step; the steps of splits past S are skipped, their loads are not.
-  {
+  if (n == RPW) {
+    // A full wave.  First pass: the W_UV,h loads ride beside the merge steps,
+    // 32 / (4 RPW) per step; the steps of splits past S are skipped, their
+    // loads are not.
     const int nc = min(kVuSplits, S);
     constexpr int kLoadsPerStep = 32 / (kVuSplits * RPW);
 #pragma unroll
@@ -393,19 +400,39 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
         if (sc < nc) merge_step(0, sc, j);
         __builtin_amdgcn_sched_barrier(0);
       }
-  }
-  for (int c0 = kVuSplits; c0 < S; c0 += kVuSplits) {
-    // The previous pass's slot reads must be complete before its slots are
-    // gathered into again.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    gather(c0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const int nc = min(kVuSplits, S - c0);
+    for (int c0 = kVuSplits; c0 < S; c0 += kVuSplits) {
+      // The previous pass's slot reads must be complete before its slots are
+      // gathered into again.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      gather(c0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const int ps = pass_splits(c0);
 #pragma unroll
-    for (int sc = 0; sc < kVuSplits; ++sc) {
-      if (sc >= nc) break;
+      for (int sc = 0; sc < kVuSplits; ++sc) {
+        if (sc >= ps) break;
 #pragma unroll
-      for (int j = 0; j < RPW; ++j) merge_step(c0, sc, j);
+        for (int j = 0; j < RPW; ++j) merge_step(c0, sc, j);
+      }
+    }
+  } else {
+    // A wave with fewer rows (or none): W_UV,h at once, then passes of
+    // kCap / n splits.
+#pragma unroll
+    for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
+    if (n > 0) {
+      for (int c0 = 0; c0 < S;) {
+        const int ps = pass_splits(c0);
+        if (c0 > 0) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          gather(c0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        for (int c = 0; c < ps; ++c)
+#pragma unroll
+          for (int j = 0; j < RPW; ++j)
+            if (j < n) merge_step(c0, c, j);
+        c0 += ps;
+      }
     }
   }
   // Merged rows (bf16) into the split-0 slots; every wave's rows must be
