@@ -270,14 +270,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
 //   lse = ln 2 (M + log2 L)
 // ---------------------------------------------------------------------------
 constexpr int kOtRow = 1040;  // bytes per latent row in LDS (512 bf16 + 16 pad)
-constexpr int kVuSplits = 4;  // splits staged per pass
 
-template <bool FUSED, int ROWS>
+template <bool FUSED, int ROWS, int SPP>
 __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
-  __shared__ __attribute__((aligned(1024))) char slots[kVuSplits * ROWS * kOtRow];
+  __shared__ __attribute__((aligned(1024))) char slots[SPP * ROWS * kOtRow];
   __shared__ float wtab[ROWS * 64];  // merge weights: per wave, row, split
   constexpr int RPW = ROWS / 4;  // batch rows per wave
-  static_assert(32 % (kVuSplits * RPW) == 0, "W_UV loads spread evenly over the first merge pass");
+  static_assert(32 % (SPP * RPW) == 0, "W_UV loads spread evenly over the first merge pass");
   const int ntiles = (a.B + ROWS - 1) / ROWS;
   const int units = kHeads * ntiles;
   const int per_xcd = (units + 7) >> 3;
@@ -297,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   // c0 .. c0 + ps - 1 of its n rows, split c0 + c row j in slot q = c n + j
   // (slot (q / RPW) ROWS + r0 + q % RPW of the array), so a wave with few
   // rows takes more splits per pass.
-  constexpr int kCap = kVuSplits * RPW;
+  constexpr int kCap = SPP * RPW;
   auto pass_splits = [&](int c0) { return min(S - c0, kCap / max(n, 1)); };
   auto slot_of = [&](int q) { return (q / RPW) * ROWS + r0 + (q % RPW); };
   // Gather one pass: one instruction per (split, row); lane l brings bytes
@@ -386,10 +385,10 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
     // A full wave.  First pass: the W_UV,h loads ride beside the merge steps,
     // 32 / (4 RPW) per step; the steps of splits past S are skipped, their
     // loads are not.
-    const int nc = min(kVuSplits, S);
-    constexpr int kLoadsPerStep = 32 / (kVuSplits * RPW);
+    const int nc = min(SPP, S);
+    constexpr int kLoadsPerStep = 32 / (SPP * RPW);
 #pragma unroll
-    for (int sc = 0; sc < kVuSplits; ++sc)
+    for (int sc = 0; sc < SPP; ++sc)
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
 #pragma unroll
@@ -400,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
         if (sc < nc) merge_step(0, sc, j);
         __builtin_amdgcn_sched_barrier(0);
       }
-    for (int c0 = kVuSplits; c0 < S; c0 += kVuSplits) {
+    for (int c0 = SPP; c0 < S; c0 += SPP) {
       // The previous pass's slot reads must be complete before its slots are
       // gathered into again.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       const int ps = pass_splits(c0);
 #pragma unroll
-      for (int sc = 0; sc < kVuSplits; ++sc) {
+      for (int sc = 0; sc < SPP; ++sc) {
         if (sc >= ps) break;
 #pragma unroll
         for (int j = 0; j < RPW; ++j) merge_step(c0, sc, j);
@@ -1087,17 +1086,25 @@ int launch_combine(const CombineArgs& a, void* stream) {
 
 int launch_value_up(const ValueUpArgs& a, void* stream) {
   // 32-row tiles, or 16 when that is what it takes to give every CU a tile.
+  // Two splits staged per pass when there are at most two (half the LDS, so
+  // two workgroups fit a CU), else four.
   const bool small = a.B <= 32;
   const int rows = small ? 16 : 32;
+  const bool two = a.o_latent != nullptr || a.S <= 2;
   const int units = kHeads * ((a.B + rows - 1) / rows);
   const dim3 grid(8 * ((units + 7) / 8));
   const hipStream_t st = (hipStream_t)stream;
   if (a.o_latent == nullptr) {
-    if (small) hipLaunchKernelGGL((value_up_kernel<true, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((value_up_kernel<true, 32>), grid, dim3(256), 0, st, a);
+    if (small) {
+      if (two) hipLaunchKernelGGL((value_up_kernel<true, 16, 2>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((value_up_kernel<true, 16, 4>), grid, dim3(256), 0, st, a);
+    } else {
+      if (two) hipLaunchKernelGGL((value_up_kernel<true, 32, 2>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((value_up_kernel<true, 32, 4>), grid, dim3(256), 0, st, a);
+    }
   } else {
-    if (small) hipLaunchKernelGGL((value_up_kernel<false, 16>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((value_up_kernel<false, 32>), grid, dim3(256), 0, st, a);
+    if (small) hipLaunchKernelGGL((value_up_kernel<false, 16, 2>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((value_up_kernel<false, 32, 2>), grid, dim3(256), 0, st, a);
   }
   return (int)hipGetLastError();
 }
