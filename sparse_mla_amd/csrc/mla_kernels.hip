@@ -213,11 +213,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
       }
       af[t][st] = tr_pair(wl + off[0], wl + off[1]);
     }
-  // The slab is in registers now; its LDS holds output tiles from here on:
-  // row r (batch row of the tile) = 512 bytes, 16-byte chunk c stored at
-  // position c ^ (r % 32), so that the global writes are whole row segments.
+  // The slab is in registers now; its LDS holds output tiles from here on,
+  // two alternating 16 KB buffers: row r (batch row of the tile) = 512
+  // bytes, 16-byte chunk c stored at position c ^ (r % 32), so that the
+  // global writes are whole row segments.  One barrier per tile: a wave
+  // stages tile t + 1 into the buffer of tile t - 1 only after the barrier of
+  // tile t, which every wave reaches after its copy-out of tile t - 1.
   __syncthreads();
-  char* ot = wt;
   for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
     if (bt0 > 0) load_q(bt0);
 #pragma unroll
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) acc[t] = mfma32(af[t][st], qb[u][st], acc[t]);
       // acc[t][v]: batch row lane % 32, column 64 w + 32 t + 8 (v / 4) + 4 hh + v % 4.
+      char* ot = wt + ((bt0 + u) & 1) * 16384;
       char* orow = ot + (lane & 31) * 512 + 8 * hh;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -248,7 +251,6 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
         if (bb < a.B)
           *reinterpret_cast<uint4*>(a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + 8 * c) = val;
       }
-      __syncthreads();
     }
   }
 }
