@@ -853,15 +853,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  // Blocks 0 and 1 go out now; the query loads resolve here with them (the
+  // Block 0 goes out now; the query loads resolve here with it (the
   // operands then count as asm-defined, so no per-use vmcnt wait, which
-  // would also drain the in-order gathers, lands in the key loop).
+  // would also drain the in-order gathers, lands in the key loop).  Block 1
+  // follows once block 0 is in: drained together, the two would hold back
+  // the first scores by a whole block's transfer.
   issue(0);
-  issue(1);
 #pragma unroll
   for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  issue(1);
 
   f32x16 prev, x_unused;
   bf16x8 pb_unused[2], pb_last[2];
