@@ -492,10 +492,11 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 // the only dependency between waves is the gathered block itself.
 //
 // Software pipeline, iteration j, after one barrier (block j has landed):
-//   A  the score chain of block j, with the softmax of block j - 1 spread
-//      over its slots (the vector work issues while each chain MFMA runs)
-//      and the gather of block j + 2 going out one line every fourth slot;
-//   B  the mix of block j - 1: 32 independent MFMAs.
+//   A  the score chain of block j: 36 dependent MFMAs and their operand
+//      reads, nothing else (any other work there holds back the next MFMA);
+//   B  the mix of block j - 1: 32 independent MFMAs, with the softmax of
+//      block j spread over their slots and the gather of block j + 2 going
+//      out one line every third slot.
 // Four row buffers: j - 1 (mix), j (scores), j + 1 and j + 2 (in flight).
 // Buffer (j + 2) % 4 last held block j - 2, mixed in iteration j - 1, which
 // every wave has finished before the barrier of iteration j.  Gathers past
@@ -511,7 +512,7 @@ constexpr int kSoftSteps = 32;              // softmax steps placed beside MFMAs
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
 constexpr int kTilePitch = 1040;            // output tile row: 512 bf16 + 16 bytes of padding
 static_assert(kHeads * kTilePitch <= kOffIdx, "the epilogue tile must stay inside the row buffers");
-static_assert(kSoftSteps <= 32, "the softmax steps must fit the score chain and the mix");
+static_assert(kSoftSteps <= 32, "the softmax steps must fit the slots of a mix");
 
 template <bool DENSE, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
@@ -800,9 +801,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // Mix of block p (rows in buffer p % 4) with this wave's P fragments pb[ks]:
   // fragment i = 16 ks + mt, one MFMA each, A fragments read four ahead.
   // With SOFT, the softmax steps of the next block (x -> pn) ride beside the
-  // MFMAs, one per MFMA.
+  // MFMAs, one per MFMA, and the gather `gn` goes out one line every third
+  // slot (a burst of gathers from four waves backs up the CU's address unit).
+  // The mix MFMAs are independent of each other, so this work delays none.
   auto mix = [&](auto soft_tag, int p, const bf16x8 (&pb)[2], f32x16& x, float cx,
-                 bf16x8 (&pn)[2]) __attribute__((always_inline)) {
+                 bf16x8 (&pn)[2], const Gather* gn) __attribute__((always_inline)) {
     constexpr bool SOFT = decltype(soft_tag)::value;
     const char LDS_AS* buf = s3 + (p % kNbuf) * kBufBytes;
     auto av_ld = [&](int i) {
@@ -819,18 +822,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       if (i + MA < 32) ring[(i + MA) % (MA + 1)] = av_ld(i + MA);
       acc[i & 15] = mfma32(ring[i % (MA + 1)], pb[i >> 4], acc[i & 15]);
       if (SOFT && i < kSoftSteps) soft_step(i, x, cx, pn);
+      if (SOFT && i % 3 == 1 && i / 3 < 9) gather_line(*gn, i / 3);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Score chain of block j into sacc.  With SOFT, the softmax steps of the
-  // previous block (x) sit one per slot after the chain's first MFMA.  The
-  // gather `gn` goes out one line every fourth slot: a burst of gathers from
-  // four waves backs up the CU's address unit and would stall the chain.
-  // Every score operand is read three slots ahead; a ring slot is reloaded
-  // after the MFMA that follows its last use has issued.
-  auto chain = [&](auto soft_tag, int j, f32x16& sacc, f32x16& x, float cx, bf16x8 (&pb)[2], const Gather& gn) __attribute__((always_inline)) {
-    constexpr bool SOFT = decltype(soft_tag)::value;
+  // Score chain of block j into sacc: 36 MFMAs, each depending on the one
+  // before, so nothing but the operand reads sits between them (other work
+  // there would hold back the next MFMA of the chain).  With `gn`, that
+  // gather goes out one line every fourth slot (block 0 only).  Every score
+  // operand is read three slots ahead; a ring slot is reloaded after the MFMA
+  // that follows its last use has issued.
+  auto chain = [&](int j, f32x16& sacc, const Gather* gn) __attribute__((always_inline)) {
     const char LDS_AS* kbuf = s3 + (j % kNbuf) * kBufBytes;
     constexpr int AH = 3;
     bf16x8 ring[AH + 1];
@@ -842,13 +845,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 36; ++k) {
-      if ((k & 3) == 0) gather_line(gn, k >> 2);
+      if (gn != nullptr && (k & 3) == 0) gather_line(*gn, k >> 2);
       const bf16x8 kf = ring[k % (AH + 1)];
       if (k == 0) sacc = mfma32_v_first(kf, qf[k]);
       else if (k == 35) mfma32_v_last(sacc, kf, qf[k]);
       else mfma32_v(sacc, kf, qf[k], ring[(k + AH) % (AH + 1)]);
       if (k + AH < 36) ring[(k + AH) % (AH + 1)] = qk_ld(k + AH);
-      if (SOFT && k >= 1 && k <= kSoftSteps) soft_step(k - 1, x, cx, pb);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -865,66 +867,50 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   __syncthreads();
   issue(1);
 
-  f32x16 prev, x_unused;
-  bf16x8 pb_unused[2], pb_last[2];
-  uint32_t vm_prev = valid_mask(0);
-  chain(std::false_type{}, 0, prev, x_unused, 1.f, pb_unused, gather_setup(2));
+  f32x16 x_unused;
+  bf16x8 pb_unused[2], pb[2];
   // Top of iteration j: block j complete (block j + 1's 9 loads are the only
   // ones behind it) and every wave done with iteration j - 1.
   auto block_barrier = [&]() __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     __syncthreads();
   };
-  int j = 1;
-  for (; j + 1 < nblk; ++j) {
+  {
+    // Block 0: its scores (block 2's gather going out beside them), then its
+    // softmax on its own.
+    const Gather g2 = gather_setup(2);
+    f32x16 sacc;
+    chain(0, sacc, &g2);
+    const uint32_t vm = valid_mask(0);
+    if (a.flags & 2u) write_scores(0, sacc, vm);
+    const float cx = prepare(sacc, vm);
+#pragma unroll
+    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sacc, cx, pb);
+  }
+  // Iteration j: the score chain of block j, then the mix of block j - 1
+  // with the softmax of block j and the gather of block j + 2 riding beside
+  // its MFMAs.  pb holds block j - 1's P on entry, block j's on exit.
+  for (int j = 1; j < nblk; ++j) {
     // Per-lane LDS bases are re-derived each iteration rather than kept as
     // dozens of hoisted base + offset sums occupying registers.
     asm volatile("" : "+v"(qk_base[0]), "+v"(qk_base[1]), "+v"(qk_base[2]), "+v"(qk_base[3]));
     asm volatile("" : "+v"(pc_base[0][0]), "+v"(pc_base[0][1]), "+v"(pc_base[1][0]), "+v"(pc_base[1][1]));
     block_barrier();
-    if (a.flags & 2u) write_scores(j - 1, prev, vm_prev);
-    const float cx = prepare(prev, vm_prev);
     const Gather gn = gather_setup(j + 2);
     const uint32_t vm = valid_mask(j);
     f32x16 sacc;
-    bf16x8 pb[2];
-    chain(std::true_type{}, j, sacc, prev, cx, pb, gn);
-    if (resc_any) rescale(alpha);
-    mix(std::false_type{}, j - 1, pb, x_unused, 1.f, pb_unused);
-    // The loop-carried scores are a copy made by explicit moves into
-    // registers of their own: were the allocator free to merge the two, it
-    // could move the accumulator into the loop registers between two chain
-    // MFMAs, reading a sum still in flight.
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float t;
-      asm volatile("v_mov_b32 %0, %1" : "=&v"(t) : "v"(sacc[v]));
-      prev[v] = t;
-    }
-    vm_prev = vm;
-  }
-  if (nblk > 1) {
-    // The last iteration, peeled: the softmax of the last block rides beside
-    // the mix of the one before.
-    block_barrier();
-    if (a.flags & 2u) write_scores(j - 1, prev, vm_prev);
-    const float cx = prepare(prev, vm_prev);
-    const uint32_t vm = valid_mask(j);
-    f32x16 sacc;
-    bf16x8 pb[2];
-    chain(std::true_type{}, j, sacc, prev, cx, pb, gather_setup(j + 2));
+    chain(j, sacc, nullptr);
+    // The factor decided by block j - 1's softmax, before its P is mixed in.
     if (resc_any) rescale(alpha);
     if (a.flags & 2u) write_scores(j, sacc, vm);
-    const float cl = prepare(sacc, vm);
-    mix(std::true_type{}, j - 1, pb, sacc, cl, pb_last);
-  } else {
-    if (a.flags & 2u) write_scores(0, prev, vm_prev);
-    const float cx = prepare(prev, vm_prev);
-#pragma unroll
-    for (int k = 0; k < kSoftSteps; ++k) soft_step(k, prev, cx, pb_last);
+    const float cx = prepare(sacc, vm);
+    bf16x8 pn[2];
+    mix(std::true_type{}, j - 1, pb, sacc, cx, pn, &gn);
+    pb[0] = pn[0];
+    pb[1] = pn[1];
   }
   if (resc_any) rescale(alpha);
-  mix(std::false_type{}, nblk - 1, pb_last, x_unused, 1.f, pb_unused);
+  mix(std::false_type{}, nblk - 1, pb, x_unused, 1.f, pb_unused, nullptr);
 
   // This lane's head: lanes l and l ^ 32 hold halves of the sum.
   {
