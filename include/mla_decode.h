@@ -65,7 +65,7 @@ typedef enum {
   MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < mla_workspace_bytes(B, num_splits)   */
   MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths     */
   MLA_ERR_HIP = 6,                 /* a HIP call failed: see mla_last_hip_error()     */
-  MLA_ERR_RANGE = 7                /* one sequence's cache span exceeds 2 GiB         */
+  MLA_ERR_RANGE = 7                /* one sequence's cache or q_pe span exceeds 2 GiB */
 } mla_status;
 
 /* Flags of mla_sparse_decode. */
@@ -148,7 +148,8 @@ int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
  * Without VALIDATE, rows with repeated indices are attended once per repeat
  * and out-of-range indices are skipped; both are caller errors.
  * Each sequence's cache span (max_len * row stride * 2 bytes, for kv and pe)
- * must be below 2 GiB (MLA_ERR_RANGE).
+ * and its q_pe span ((127 * q_pe_sh + 64) * 2 bytes) must be below 2 GiB
+ * (MLA_ERR_RANGE).
  */
 int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
                       const void* kv, int64_t kv_sb, int64_t kv_st,

@@ -46,7 +46,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_workspace_bytes()";
     case MLA_ERR_UNSUPPORTED: return "stride smaller than the fixed row width";
     case MLA_ERR_HIP: return "HIP runtime error (see mla_last_hip_error)";
-    case MLA_ERR_RANGE: return "a sequence's cache span exceeds 2 GiB";
+    case MLA_ERR_RANGE: return "a sequence's cache or q_pe span exceeds 2 GiB";
     default: return "unknown status";
   }
 }
@@ -129,7 +129,8 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
     return MLA_ERR_ALIGNMENT;
   if (kv_st < MLA_LATENT_DIM || pe_st < MLA_ROPE_DIM) return MLA_ERR_UNSUPPORTED;
   const int64_t span_limit = ((int64_t)1 << 31) - 1;
-  if ((int64_t)max_len * kv_st * 2 > span_limit || (int64_t)max_len * pe_st * 2 > span_limit)
+  if ((int64_t)max_len * kv_st * 2 > span_limit || (int64_t)max_len * pe_st * 2 > span_limit ||
+      ((int64_t)(MLA_HEADS - 1) * q_pe_sh + MLA_ROPE_DIM) * 2 > span_limit)
     return MLA_ERR_RANGE;
   if (num_splits == 1) {
     if (!o_latent) return MLA_ERR_NULL_POINTER;

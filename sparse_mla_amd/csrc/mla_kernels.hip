@@ -81,6 +81,13 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t vo
                : "s"(lds_base), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+// The same with 4 bytes per lane (lane l lands at lds_base + 4 l).
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -507,7 +514,8 @@ constexpr int kBlk = 32;                    // keys per block
 constexpr int kNbuf = 4;                    // row buffers
 constexpr int kBufBytes = 72 * kBlk * 16;   // 36864: one block of rows
 constexpr int kOffIdx = kNbuf * kBufBytes;  // int [kIdxCap]
-constexpr int kDecodeLds = kOffIdx + kIdxCap * 4;
+constexpr int kOffLen = kOffIdx + kIdxCap * 4;  // int [4][64]: the sequence length, per wave
+constexpr int kDecodeLds = kOffLen + 4 * 64 * 4;
 constexpr int kSoftSteps = 32;              // softmax steps placed beside MFMAs
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
 constexpr int kTilePitch = 1040;            // output tile row: 512 bf16 + 16 bytes of padding
@@ -535,51 +543,82 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   constexpr bool dense = DENSE;
   const bool validate = (a.flags & 1u) != 0;
-  const int Lb = min(max(a.seq_lens[b], 0), a.max_len);
   const int s0 = s * a.chunk;
   const int s1 = min(a.k_max, s0 + a.chunk);
   const int nslot = max(0, s1 - s0);
   const int nblk = (nslot + kBlk - 1) / kBlk;
 
-  // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B layout.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
+  // Score-read offsets: row lane % 32 of a tile laid out like a gathered
+  // block, chunk 2 st + hh of line st / 4.
+  uint32_t qk_base[4];
+  {
+    const uint32_t key = (uint32_t)(lane & 31);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      qk_base[s4] = key * 128u + (((uint32_t)(2 * s4 + hh)) ^ seg_swz(key)) * 16u;
+  }
+
+  // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B
+  // layout.  Read straight from HBM, each load would touch 32 rows for 32
+  // bytes apiece; instead each wave moves its 32 heads' rows into its own row
+  // buffer with whole-line LDS-DMA (8 lanes per 128-byte line, laid out and
+  // swizzled like a gathered block: head row r as key r) and reads the
+  // operand back with the score reads.  The B layout (n = lane % 32, k = 8
+  // (lane / 32) + v) is the A layout of the score operand, so the same reads
+  // serve.
   bf16x8 qf[36];
-  auto load_query = [&]() __attribute__((always_inline)) {
-    const uint16_t* qa = a.q_abs + ((int64_t)b * kHeads + head) * kLatent + 8 * hh;
+  auto stage_query = [&]() __attribute__((always_inline)) {
+    const i32x4 rq = buffer_rsrc(a.q_abs + (int64_t)b * kHeads * kLatent, (uint32_t)(kHeads * kLatent * 2));
+    const i32x4 rp = buffer_rsrc(a.q_pe + (int64_t)b * a.q_pe_sb,
+                                 (uint32_t)(((int64_t)(kHeads - 1) * a.q_pe_sh + kRope) * 2));
+    const uint32_t qdst = lds0 + (uint32_t)(wave * kBufBytes);
 #pragma unroll
-    for (int st = 0; st < 32; ++st) qf[st] = ld8(qa + 16 * st);
-    const uint16_t* qp = a.q_pe + (int64_t)b * a.q_pe_sb + (int64_t)head * a.q_pe_sh + 8 * hh;
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t r = (uint32_t)(8 * g + (lane >> 3));
+      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
+      const uint32_t hrow = (uint32_t)(32 * wave) + r;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) qf[32 + st] = ld8(qp + 16 * st);
+      for (int m = 0; m < 8; ++m)
+        dma16(rq, qdst + (uint32_t)(m * kBlk * 128 + 8 * g * 128), hrow * (uint32_t)(kLatent * 2) + (uint32_t)(m * 128) + q16);
+      dma16(rp, qdst + (uint32_t)(8 * kBlk * 128 + 8 * g * 128), hrow * (uint32_t)(a.q_pe_sh * 2) + q16);
+    }
   };
+  auto read_query = [&]() __attribute__((always_inline)) {
+    const char LDS_AS* qb = s3 + wave * kBufBytes;
+#pragma unroll
+    for (int st = 0; st < 36; ++st)
+      qf[st] = *(const bf16x8 LDS_AS*)(qb + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
+  };
+
+  // Every load of the prologue is an LDS-DMA: the sequence length (lane 0
+  // of each wave; the other lanes read past the 4-byte range and land
+  // zeros), this split's index slots (slot i lands at sidx[i]; slots past
+  // nslot read as zeros and are masked below), then the query rows.  With no
+  // compiler-visible load the only waits are the explicit ones below (a
+  // compiler-placed wait for an ordinary load would also drain the query
+  // rows; a scalar load of the length would be waited on with the kernel
+  // arguments, before anything else goes out).
+  dma4(buffer_rsrc(a.seq_lens + b, 4u), lds0 + (uint32_t)(kOffLen + 256 * wave), 4u * (uint32_t)lane);
+  if constexpr (!dense) {
+    // 4 bytes per lane, so that the range check (nslot slots) is per slot.
+    const i32x4 ri = buffer_rsrc(a.indices + (int64_t)b * a.k_max + s0, (uint32_t)nslot * 4u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dma4(ri, lds0 + (uint32_t)(kOffIdx + 4 * (256 * wave + 64 * k)), 4u * (uint32_t)(256 * wave + 64 * k + lane));
+  }
+  stage_query();
+  asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+  const int Lb = __builtin_amdgcn_readfirstlane(
+      min(max(*(const volatile int LDS_AS*)(s3 + kOffLen + 256 * wave), 0), a.max_len));
 
   // Stage this split's index slots as cache rows (-1 = masked).  The same
   // predicate decides validity, the attended bitmap and the device checks.
-  // Thread t owns slots 4 t .. 4 t + 3 of each 1024-slot pass; the query
-  // loads go out after the index loads and stay in flight while the indices
-  // are staged (vmcnt retires in order).
   if constexpr (!dense) {
-    constexpr int kPass = 4 * 256;
-    int4 raw[kIdxCap / kPass];
-#pragma unroll
-    for (int ps = 0; ps < kIdxCap / kPass; ++ps) {
-      const int i0 = ps * kPass + 4 * tid;
-      const int64_t base = (int64_t)b * a.k_max + s0 + i0;
-      if (i0 + 3 < nslot && (base & 3) == 0) {
-        raw[ps] = *reinterpret_cast<const int4*>(a.indices + base);
-      } else {
-        raw[ps].x = i0 + 0 < nslot ? a.indices[base + 0] : -1;
-        raw[ps].y = i0 + 1 < nslot ? a.indices[base + 1] : -1;
-        raw[ps].z = i0 + 2 < nslot ? a.indices[base + 2] : -1;
-        raw[ps].w = i0 + 3 < nslot ? a.indices[base + 3] : -1;
-      }
-    }
-    load_query();
-    asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
-#pragma unroll
-    for (int ps = 0; ps < kIdxCap / kPass; ++ps) {
-      const int i0 = ps * kPass + 4 * tid;
-      if (i0 >= nblk * kBlk) continue;
-      int r[4] = {raw[ps].x, raw[ps].y, raw[ps].z, raw[ps].w};
+    {
+      const int i0 = 4 * tid;
+      const int4 raw = *reinterpret_cast<const int4*>(sidx + i0);
+      int r[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = r[e];
@@ -597,7 +636,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       *reinterpret_cast<int4*>(sidx + i0) = make_int4(r[0], r[1], r[2], r[3]);
     }
   } else {
-    load_query();
     if (validate) {
       for (int i = tid; i < nslot; i += 256) {
         const int t = s0 + i;
@@ -605,6 +643,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       }
     }
   }
+  // The query rows are in; every wave reads its operand before the barrier,
+  // after which block 0 is gathered over wave 0's rows.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  read_query();
+#pragma unroll
+  for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
   __syncthreads();
 
   uint16_t* dst = !SPLIT ? a.o_latent + (int64_t)b * kHeads * kLatent
@@ -641,8 +685,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const uint32_t kv_rb = (uint32_t)(a.kv_st * 2), pe_rb = (uint32_t)(a.pe_st * 2);
   const i32x4 rkv = buffer_rsrc(a.kv + (int64_t)b * a.kv_sb, (uint32_t)Lb * kv_rb);
   const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)b * a.pe_sb, (uint32_t)Lb * pe_rb);
-  const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
-
   // Gather block p into buffer p % 4: wave w moves keys 8 w .. 8 w + 7, all
   // 9 lines; lane l takes key 8 w + l / 8 and 16-byte position l % 8.
   struct Gather {
@@ -669,14 +711,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     for (int m = 0; m < 9; ++m) gather_line(g, m);
   };
 
-  // Score-read offsets: key lane % 32, chunk 2 st + hh (line st / 4).
-  uint32_t qk_base[4];
-  {
-    const uint32_t key = (uint32_t)(lane & 31);
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-      qk_base[s4] = key * 128u + (((uint32_t)(2 * s4 + hh)) ^ seg_swz(key)) * 16u;
-  }
   // Transpose-read offsets (mix A operand, column tile mt, k-step ks): in
   // each 16-lane group (gm = group & 1) source lane i reads key
   // 16 ks + 8 r + 4 hh + i / 4 for the fragment's two reads r = 0, 1, and
@@ -855,14 +889,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  // Block 0 goes out now; the query loads resolve here with it (the
-  // operands then count as asm-defined, so no per-use vmcnt wait, which
-  // would also drain the in-order gathers, lands in the key loop).  Block 1
-  // follows once block 0 is in: drained together, the two would hold back
-  // the first scores by a whole block's transfer.
+  // Block 0 goes out now, block 1 once block 0 is in: drained together, the
+  // two would hold back the first scores by a whole block's transfer.
   issue(0);
-#pragma unroll
-  for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   issue(1);

@@ -109,6 +109,7 @@ def _decode(lib, **kw):
     (dict(kv_st=504, pe_st=504), UNSUP),
     (dict(pe_st=56), UNSUP),
     (dict(max_len=2000000, kv_sb=576 * 2000000, pe_sb=576 * 2000000), RANGE),
+    (dict(q_pe_sh=8 * 1100000), RANGE),               # q_pe span of one sequence > 2 GiB
     (dict(o_lat=None), NULLP),
     (dict(S=2, ws=None), NULLP),
     (dict(S=2, ws=FAKE, ws_bytes=100), WS),
