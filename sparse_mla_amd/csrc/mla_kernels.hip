@@ -513,13 +513,20 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 constexpr int kBlk = 32;                    // keys per block
 constexpr int kNbuf = 4;                    // row buffers
 constexpr int kBufBytes = 72 * kBlk * 16;   // 36864: one block of rows
-constexpr int kOffIdx = kNbuf * kBufBytes;  // int [kIdxCap]
+// Query staging in the prologue: lines 7 and 8 of each wave's 32 head rows
+// in buffer 0 (8 KB per wave), lines 0 .. 6 from buffer 1 on (28 KB per
+// wave, 4 KB past buffer 3), so that block 0 can be gathered into buffer 0
+// while the bulk of the query is still arriving.
+constexpr int kOffQ = kBufBytes;
+constexpr int kQWave = 7 * kBlk * 128;
+constexpr int kOffIdx = kOffQ + 4 * kQWave;  // int [kIdxCap]
 constexpr int kOffLen = kOffIdx + kIdxCap * 4;  // int [4][64]: the sequence length, per wave
 constexpr int kDecodeLds = kOffLen + 4 * 64 * 4;
 constexpr int kSoftSteps = 32;              // softmax steps placed beside MFMAs
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
 constexpr int kTilePitch = 1040;            // output tile row: 512 bf16 + 16 bytes of padding
-static_assert(kHeads * kTilePitch <= kOffIdx, "the epilogue tile must stay inside the row buffers");
+static_assert(kHeads * kTilePitch <= kNbuf * kBufBytes, "the epilogue tile must stay inside the row buffers");
+static_assert(kOffIdx >= kNbuf * kBufBytes, "the index list must not overlap the row buffers");
 static_assert(kSoftSteps <= 32, "the softmax steps must fit the slots of a mix");
 
 template <bool DENSE, bool SPLIT>
@@ -561,44 +568,51 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Query operand [q~ (512) | q_pe (64)] for this lane's head, in MFMA B
   // layout.  Read straight from HBM, each load would touch 32 rows for 32
-  // bytes apiece; instead each wave moves its 32 heads' rows into its own row
-  // buffer with whole-line LDS-DMA (8 lanes per 128-byte line, laid out and
-  // swizzled like a gathered block: head row r as key r) and reads the
-  // operand back with the score reads.  The B layout (n = lane % 32, k = 8
-  // (lane / 32) + v) is the A layout of the score operand, so the same reads
-  // serve.
+  // bytes apiece; instead each wave moves its 32 heads' rows into LDS with
+  // whole-line LDS-DMA (8 lanes per 128-byte line, lines laid out and
+  // swizzled like those of a gathered block: head row r as key r) and reads
+  // the operand back with the score reads.  The B layout (n = lane % 32,
+  // k = 8 (lane / 32) + v) is the A layout of the score operand, so the same
+  // reads serve.  Lines 7 and 8 go to buffer 0, lines 0 .. 6 to the region
+  // at kOffQ; line m of the tile at `base` + m * 4 KB either way.
   bf16x8 qf[36];
-  auto stage_query = [&]() __attribute__((always_inline)) {
+  auto query_base = [&](int m) __attribute__((always_inline)) -> uint32_t {
+    return m >= 7 ? (uint32_t)(8192 * wave + (m - 7) * kBlk * 128)
+                  : (uint32_t)(kOffQ + kQWave * wave + m * kBlk * 128);
+  };
+  auto stage_query = [&](int m0, int m1) __attribute__((always_inline)) {
     const i32x4 rq = buffer_rsrc(a.q_abs + (int64_t)b * kHeads * kLatent, (uint32_t)(kHeads * kLatent * 2));
     const i32x4 rp = buffer_rsrc(a.q_pe + (int64_t)b * a.q_pe_sb,
                                  (uint32_t)(((int64_t)(kHeads - 1) * a.q_pe_sh + kRope) * 2));
-    const uint32_t qdst = lds0 + (uint32_t)(wave * kBufBytes);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t r = (uint32_t)(8 * g + (lane >> 3));
       const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
       const uint32_t hrow = (uint32_t)(32 * wave) + r;
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-        dma16(rq, qdst + (uint32_t)(m * kBlk * 128 + 8 * g * 128), hrow * (uint32_t)(kLatent * 2) + (uint32_t)(m * 128) + q16);
-      dma16(rp, qdst + (uint32_t)(8 * kBlk * 128 + 8 * g * 128), hrow * (uint32_t)(a.q_pe_sh * 2) + q16);
+      for (int m = m0; m < m1; ++m) {
+        const uint32_t dst = lds0 + query_base(m) + (uint32_t)(8 * g * 128);
+        if (m < 8) dma16(rq, dst, hrow * (uint32_t)(kLatent * 2) + (uint32_t)(m * 128) + q16);
+        else dma16(rp, dst, hrow * (uint32_t)(a.q_pe_sh * 2) + q16);
+      }
     }
   };
-  auto read_query = [&]() __attribute__((always_inline)) {
-    const char LDS_AS* qb = s3 + wave * kBufBytes;
+  auto read_query = [&](int st0, int st1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int st = 0; st < 36; ++st)
-      qf[st] = *(const bf16x8 LDS_AS*)(qb + qk_base[st & 3] + (uint32_t)((st >> 2) * kBlk * 128));
+    for (int st = st0; st < st1; ++st)
+      qf[st] = *(const bf16x8 LDS_AS*)(s3 + query_base(st >> 2) + qk_base[st & 3]);
   };
 
-  // Every load of the prologue is an LDS-DMA: the sequence length (lane 0
-  // of each wave; the other lanes read past the 4-byte range and land
-  // zeros), this split's index slots (slot i lands at sidx[i]; slots past
-  // nslot read as zeros and are masked below), then the query rows.  With no
+  // Every load of the prologue is an LDS-DMA: query lines 7 and 8 (8 per
+  // wave), the sequence length (lane 0 of each wave; the other lanes read
+  // past the 4-byte range and land zeros), this split's index slots (slot i
+  // lands at sidx[i]; slots past nslot read as zeros and are masked below),
+  // then query lines 0 .. 6 (28 per wave).  With no
   // compiler-visible load the only waits are the explicit ones below (a
   // compiler-placed wait for an ordinary load would also drain the query
   // rows; a scalar load of the length would be waited on with the kernel
   // arguments, before anything else goes out).
+  stage_query(7, 9);
   dma4(buffer_rsrc(a.seq_lens + b, 4u), lds0 + (uint32_t)(kOffLen + 256 * wave), 4u * (uint32_t)lane);
   if constexpr (!dense) {
     // 4 bytes per lane, so that the range check (nslot slots) is per slot.
@@ -607,8 +621,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     for (int k = 0; k < 4; ++k)
       dma4(ri, lds0 + (uint32_t)(kOffIdx + 4 * (256 * wave + 64 * k)), 4u * (uint32_t)(256 * wave + 64 * k + lane));
   }
-  stage_query();
-  asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+  stage_query(0, 7);
+  asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+  read_query(28, 36);
   const int Lb = __builtin_amdgcn_readfirstlane(
       min(max(*(const volatile int LDS_AS*)(s3 + kOffLen + 256 * wave), 0), a.max_len));
 
@@ -643,17 +658,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       }
     }
   }
-  // The query rows are in; every wave reads its operand before the barrier,
-  // after which block 0 is gathered over wave 0's rows.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  read_query();
+  // Every wave has read its query lines 7 and 8 out of buffer 0 before this
+  // barrier, after which block 0 is gathered there.
 #pragma unroll
-  for (int st = 0; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
+  for (int st = 28; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
   __syncthreads();
 
   uint16_t* dst = !SPLIT ? a.o_latent + (int64_t)b * kHeads * kLatent
                              : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
   if (nblk == 0) {
+    // The query rows may still be landing in this workgroup's LDS.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // No slot in this split: the normalised mix is NaN with S == 1 (an empty
     // selection); with several splits the (unnormalised) sum is 0 and the
     // merge gives it no weight.  (max, sum) = (-inf, 0).  Everything below
@@ -889,9 +904,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     }
   };
 
-  // Block 0 goes out now, block 1 once block 0 is in: drained together, the
-  // two would hold back the first scores by a whole block's transfer.
+  // Block 0 goes out now; the rest of the query (its 28 loads are the only
+  // ones ahead of block 0's 9) is read while block 0 arrives.  Block 1 goes
+  // out once block 0 is in and every wave is done with the query region:
+  // drained together, the two would hold back the first scores by a whole
+  // block's transfer.
   issue(0);
+  asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  read_query(0, 28);
+#pragma unroll
+  for (int st = 0; st < 28; ++st) asm volatile("" : "+v"(qf[st]));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   issue(1);
