@@ -188,7 +188,8 @@ int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
  * reads its O~ operand merged on the fly from the split partials in
  * `workspace` (the same merge as mla_combine), so O~ is never stored.
  * out as in mla_value_up; lse fp32 [B][128] (may be NULL); status_dev as in
- * mla_combine (may be NULL).
+ * mla_combine (may be NULL).  MLA_ERR_RANGE when the partials' (max, sum)
+ * array (num_splits * B * 128 * 8 bytes) exceeds 2 GiB.
  */
 int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
                          const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh, float* lse,

@@ -226,6 +226,7 @@ int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int3
     return MLA_ERR_ALIGNMENT;
   if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
   const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  if (units * 8 > (size_t)INT32_MAX) return MLA_ERR_RANGE;  // (max, sum) addressed with 32-bit offsets
   mla::ValueUpArgs a = {};
   a.o_latent = nullptr;
   a.wkv_b = static_cast<const uint16_t*>(wkv_b);

@@ -285,6 +285,10 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   __shared__ __attribute__((aligned(1024))) char slots[SPP * ROWS * kOtRow];
   __shared__ float wtab[ROWS * 64];  // merge weights: per wave, row, split
   constexpr int RPW = ROWS / 4;  // batch rows per wave
+  // (max, sum) per wave, row and split: the table DMAs write 32 entries
+  // each, one DMA when SPP == 2 (at most two splits), up to 2 RPW otherwise.
+  constexpr int kMlWave = SPP == 2 ? 32 : RPW * 64;
+  __shared__ float2 mltab[FUSED ? 4 * kMlWave : 1];
   static_assert(32 % (SPP * RPW) == 0, "W_UV loads spread evenly over the first merge pass");
   const int ntiles = (a.B + ROWS - 1) / ROWS;
   const int units = kHeads * ntiles;
@@ -323,51 +327,71 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
               (uint32_t)j * kHeads * kLatent * 2u + 16u * (uint32_t)lane);
     }
   };
-  // Order: this wave's first partial rows and its splits' (max, sum); once
-  // they have landed, W_UV,h, spread over the steps of the first merge pass
-  // (issued at once, the 32 loads per lane stall the wave's issue until most
-  // of them have returned, and the merge would wait behind them).
-  gather(0);
+  // Wait until at most k vector-memory operations are outstanding, k rounded
+  // down to a multiple of 8 (waiting longer is always correct).
+  auto wait_vm_le = [&](int k) __attribute__((always_inline)) {
+    if (k >= 56) asm volatile("s_waitcnt vmcnt(56)" ::: "memory");
+    else if (k >= 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+    else if (k >= 40) asm volatile("s_waitcnt vmcnt(40)" ::: "memory");
+    else if (k >= 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    else if (k >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (k >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (k >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
 
-  // (max, sum) loads, lane-parallel: in pass q lane l takes row
-  // j = q R + l / G and split s = l % G, with G = S rounded up to a power of
-  // two and R = 64 / G rows per pass.
+  // Order of the loads: the (max, sum) of this wave's rows and splits, the
+  // first pass of partial rows (split-major), then W_UV,h once the merge
+  // weights are computed, spread over the steps of the first merge pass
+  // (issued at once, the 32 loads per lane stall the wave's issue until
+  // most of them have returned).  vmcnt retires in order, so each split is
+  // merged as soon as its rows are in while the later ones still arrive.
+  // The (max, sum) come by LDS-DMA too (4 bytes per lane; entry (j G + sp)
+  // of the wave's table holds row j, split sp; lanes of splits past S or of
+  // rows past the batch land zeros or unused values): a compiler-visible load
+  // would get a compiler-placed wait that also drains the partial rows.
   const int G = S <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(S - 1)));
   const int gsh = __builtin_ctz((unsigned)G);
   const int R = 64 >> gsh;
-  constexpr int kMaxPasses = RPW;  // G = 64
-  float2 mlv[kMaxPasses];
+  const int nml = (RPW * 2 * G + 63) >> 6;  // table DMAs: 64 entries each
+  float2* mlt = mltab + (FUSED ? wave * kMlWave : 0);
   if constexpr (FUSED) {
-#pragma unroll
-    for (int q = 0; q < kMaxPasses; ++q) {
-      mlv[q] = float2{-INFINITY, 0.f};
-      if (q * R >= RPW) continue;
-      const int j = q * R + (lane >> gsh), sp = lane & (G - 1);
-      if (j < RPW && sp < S) {
-        const int64_t bh = (int64_t)min(b0 + r0 + j, a.B - 1) * kHeads + h;
-        mlv[q] = *reinterpret_cast<const float2*>(a.part_ml + ((int64_t)sp * sstride + bh) * 2);
-      }
+    const int64_t bh0 = (int64_t)min(b0 + r0, a.B - 1) * kHeads + h;
+    const float* mlb = a.part_ml + bh0 * 2;
+    const uint32_t rng = (uint32_t)(((int64_t)S * sstride - bh0) * 8);
+    const i32x4 rml = buffer_rsrc(mlb, rng);
+    const uint32_t mdst = (uint32_t)(uintptr_t)(char LDS_AS*)mlt;
+    for (int i = 0; i < nml; ++i) {
+      const int e = 64 * i + lane;  // entry index: (j G + sp) 2 + f
+      const int j = e >> (gsh + 1), sp = (e >> 1) & (G - 1), f = e & 1;
+      const uint32_t off = (sp < S && j < RPW) ? (uint32_t)(sp * sstride * 8 + j * kHeads * 8 + 4 * f) : 0xfffffff0u;
+      dma4(rml, mdst + 256u * (uint32_t)i, off);
     }
   }
+  gather(0);
+  const int ps0 = pass_splits(0);
+  const int g0 = n > 0 ? ps0 * n : 0;  // partial-row loads of the first pass
+  wait_vm_le(g0);
 
-  // The partial rows (this wave's own LDS slots) and (max, sum) are in.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
   bf16x8 wf[32];
 
   // Merge weights g_s = 2^(m_s - M) / L of the row, from a group max and a
   // group sum over the row's G lanes, into a per-wave table (an all -inf row
-  // gets NaN weights: an empty selection, as in mla_combine).
+  // gets NaN weights: an empty selection, as in mla_combine).  In pass q lane
+  // l takes row j = q R + l / G and split s = l % G: table entries 64 q + l.
   float* wt = reinterpret_cast<float*>(wtab) + wave * RPW * 64;
   if constexpr (FUSED) {
+    constexpr int kMaxPasses = RPW;  // G = 64
 #pragma unroll
     for (int q = 0; q < kMaxPasses; ++q) {
       if (q * R >= RPW) continue;
       const int j = q * R + (lane >> gsh), sp = lane & (G - 1);
-      float M = mlv[q].x;
+      const float2 ml = (j < RPW && sp < S) ? mlt[64 * q + lane] : float2{-INFINITY, 0.f};
+      float M = ml.x;
       for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-      const float e = (mlv[q].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mlv[q].x - M);
-      float L = e * mlv[q].y;
+      const float e = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+      float L = e * ml.y;
       for (int o = 1; o < G; o <<= 1) L += __shfl_xor(L, o);
       if (j < RPW && sp < S) wt[j * 64 + sp] = L > 0.f ? e / L : __builtin_nanf("");
       if (j < RPW && sp == 0 && r0 + j < nrows) {
@@ -391,13 +415,14 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
     for (int k = 0; k < 8; ++k) v[j][k] += gs * (float)x[k];
   };
   if (n == RPW) {
-    // A full wave.  First pass: the W_UV,h loads ride beside the merge steps,
-    // 32 / (4 RPW) per step; the steps of splits past S are skipped, their
-    // loads are not.
-    const int nc = min(SPP, S);
+    // A full wave.  First pass: split sc's rows are the oldest loads left
+    // once (ps0 - 1 - sc) RPW partial loads and the W_UV,h loads issued so
+    // far are outstanding; the W_UV,h loads ride beside the merge steps,
+    // 32 / (SPP RPW) per step (those of steps past the pass still go out).
     constexpr int kLoadsPerStep = 32 / (SPP * RPW);
 #pragma unroll
-    for (int sc = 0; sc < SPP; ++sc)
+    for (int sc = 0; sc < SPP; ++sc) {
+      if (sc < ps0) wait_vm_le((ps0 - 1 - sc) * RPW + sc * RPW * kLoadsPerStep);
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
 #pragma unroll
@@ -405,9 +430,10 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
           const int st = (sc * RPW + j) * kLoadsPerStep + u;
           wf[st] = ld8(w + 16 * st);
         }
-        if (sc < nc) merge_step(0, sc, j);
+        if (sc < ps0) merge_step(0, sc, j);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
     for (int c0 = SPP; c0 < S; c0 += SPP) {
       // The previous pass's slot reads must be complete before its slots are
       // gathered into again.
@@ -425,6 +451,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   } else {
     // A wave with fewer rows (or none): W_UV,h at once, then passes of
     // kCap / n splits.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
     if (n > 0) {
