@@ -107,8 +107,9 @@ size_t mla_workspace_bytes(int32_t B, int32_t num_splits);
  *           (d contiguous; the [B,1,128,128] layout has sb = 16384, sh = 128).
  *   wkv_b   bf16 [32768][512], contiguous.
  *   q_abs   bf16 [B][128][512], contiguous (written).
- * Requires 1 <= B <= 65536, 16-byte aligned bases, strides multiples of 8.
- * fp32 accumulation, one rounding to bf16.
+ * Requires 1 <= B <= 65536, 16-byte aligned bases, strides multiples of 8,
+ * non-negative strides and (B - 1) * q_nope_sb * 2 + 256 below 4 GiB
+ * (MLA_ERR_RANGE).  fp32 accumulation, one rounding to bf16.
  */
 int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
                  const void* wkv_b, void* q_abs, int32_t B, void* stream);

@@ -97,6 +97,9 @@ int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
   if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_abs) || !stride8(q_nope_sb) ||
       !stride8(q_nope_sh))
     return MLA_ERR_ALIGNMENT;
+  // One head's rows are read with 32-bit byte offsets.
+  if (q_nope_sb < 0 || q_nope_sh < 0 || ((int64_t)(B - 1) * q_nope_sb + MLA_NOPE_DIM) * 2 > (int64_t)UINT32_MAX)
+    return MLA_ERR_RANGE;
   mla::AbsorbArgs a;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_sb = q_nope_sb;

@@ -158,106 +158,166 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 // ---------------------------------------------------------------------------
 // absorb: q_abs[b][h][c] = sum_d q_nope[b][h][d] W_UK,h[d][c]
 // Workgroup = (head, 256-column half): 256 workgroups, each streaming its
-// 64 KB slab of W_UK once and looping over 32-row batch tiles.  W_UK is
-// stored [d][c] (c contiguous)
-// while d is the reduction index, so the 128 x 256 slab (64 KB) is moved into
-// LDS by LDS-DMA -- 8 lanes per 128-byte line, line m of row d at segment
+// 64 KB slab of W_UK once.  W_UK is stored [d][c] (c contiguous) while d is
+// the reduction index, so the 128 x 256 slab is moved into LDS by LDS-DMA --
+// 8 lanes per 128-byte line, line m (64 columns) of row d at segment
 // (m * 128 + d), chunk q at 16-byte position q ^ 2 (d % 4), which keeps the
-// transpose reads conflict-free -- and read back as K-strided MFMA fragments.
-// Wave w owns columns 64 w .. 64 w + 63 of the half (two 32-column tiles):
-// M = c, N = b, K = d.  The first query tiles load while the slab is in flight.
+// transpose reads conflict-free -- and read back as K-strided MFMA
+// fragments.  The half is done as two 128-column quarters (lines 0-1, then
+// 2-3), each a 32 KB region: the first quarter's products and stores run
+// while the second quarter's slab is still arriving.  In quarter Q wave w
+// owns columns 128 Q + 32 w .. + 31: M = c, N = b, K = d.
+// The query rows (B operand) also come by LDS-DMA, four 32-row batch tiles
+// at a time, laid out like a gathered block of the decode (row r of a tile,
+// line m = d / 64 at m * 4 KB + r * 128, chunk swizzled by seg_swz(r)), so
+// each load moves whole lines; read directly, each would touch 32 rows for
+// 32 bytes apiece.  With no compiler-visible load, every wait is explicit.
 // ---------------------------------------------------------------------------
+constexpr int kAbsQ = 32 * 1024;             // one quarter of the slab
+constexpr int kAbsQTile = 2 * 32 * 128;      // one 32-row query tile (8 KB)
+constexpr int kAbsLds = 2 * kAbsQ + 4 * kAbsQTile;
+
 __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
-  __shared__ __attribute__((aligned(1024))) char wt[4 * kNope * 128];
+  __shared__ __attribute__((aligned(1024))) char wt[kAbsLds];
   const int h = blockIdx.x & (kHeads - 1);
   const int ch = blockIdx.x >> 7;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, i16 = lane & 15, gm = (lane >> 4) & 1;
   const char LDS_AS* wl = (const char LDS_AS*)wt;
-  {
-    const i32x4 rw = buffer_rsrc(a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ch * 256,
-                                 (uint32_t)((kNope - 1) * kLatent * 2 + 512));
-    const uint32_t lds0 = (uint32_t)(uintptr_t)wl;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)wl;
+  const uint32_t qt0 = lds0 + (uint32_t)(2 * kAbsQ);  // query tiles
+
+  // Quarter Q of the slab: lines 2Q and 2Q + 1, 32 instructions, 8 per wave.
+  const i32x4 rw = buffer_rsrc(a.wkv_b + (size_t)h * kRowsPerHead * kLatent + ch * 256,
+                               (uint32_t)((kNope - 1) * kLatent * 2 + 512));
+  auto stage_slab = [&](int Q) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int ins = wave * 16 + k;                   // line ins / 16, rows 8 (ins % 16) + 0..7
-      const uint32_t d = (uint32_t)(((ins & 15) << 3) + (lane >> 3));
+    for (int k = 0; k < 8; ++k) {
+      const int qi = 8 * wave + k;                      // 0 .. 31
+      const int m = 2 * Q + (qi >> 4), rg = qi & 15;     // line, row group
+      const uint32_t d = (uint32_t)((rg << 3) + (lane >> 3));
       const uint32_t q = (uint32_t)(lane & 7) ^ (2u * (d & 3u));
-      dma16(rw, lds0 + (uint32_t)ins * 1024u, d * (uint32_t)(kLatent * 2) + (uint32_t)(ins >> 4) * 128u + q * 16u);
-    }
-  }
-  // A operand (the slab, as K-strided fragments) is the same for every batch
-  // tile: read it once.  Query tiles are loaded four at a time.
-  const int nbt = (a.B + 31) / 32;
-  bf16x8 qb[4][8];
-  auto load_q = [&](int bt0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (bt0 + u >= nbt) break;  // uniform: tiles past the batch are not loaded
-      // Rows past B load row B-1: they only feed output columns that are
-      // never stored, and unconditional loads keep all of them in flight.
-      const int bb = min((bt0 + u) * 32 + (lane & 31), a.B - 1);
-      const uint16_t* q = a.q_nope + (int64_t)bb * a.q_sb + (int64_t)h * a.q_sh + 8 * hh;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) qb[u][st] = ld8(q + 16 * st);
+      dma16(rw, lds0 + (uint32_t)(m * 128 + 8 * rg) * 128u, d * (uint32_t)(kLatent * 2) + (uint32_t)m * 128u + q * 16u);
     }
   };
-  load_q(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  bf16x8 af[2][8];
+  // Query tiles bt0 .. bt0 + 3 (those that exist): 8 instructions per tile,
+  // 2 per wave; rows past B load row B - 1 (their columns are never stored).
+  const int nbt = (a.B + 31) / 32;
+  auto stage_q = [&](int bt0) __attribute__((always_inline)) {
+    const i32x4 rq = buffer_rsrc(a.q_nope + (int64_t)h * a.q_sh, (uint32_t)(((int64_t)(a.B - 1) * a.q_sb + kNope) * 2));
 #pragma unroll
-  for (int st = 0; st < 8; ++st)
+    for (int u = 0; u < 4; ++u) {
+      if (bt0 + u >= nbt) break;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int k = 0; k < 2; ++k) {
+        const int qi = 2 * wave + k;                     // 0 .. 7
+        const int m = qi >> 2, g = qi & 3;               // line, row group
+        const uint32_t r = (uint32_t)(8 * g + (lane >> 3));
+        const int bb = min((bt0 + u) * 32 + (int)r, a.B - 1);
+        const uint32_t c16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
+        dma16(rq, qt0 + (uint32_t)(u * kAbsQTile + m * 32 * 128 + 8 * g * 128),
+              (uint32_t)((int64_t)bb * a.q_sb * 2) + (uint32_t)(m * 128) + c16);
+      }
+    }
+  };
+  auto qk_off = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    const uint32_t r = (uint32_t)(lane & 31);
+    return (uint32_t)((st >> 2) * 32 * 128) + r * 128u + (((uint32_t)(2 * (st & 3) + hh)) ^ seg_swz(r)) * 16u;
+  };
+  // Slab fragments of quarter Q for this wave (A operand, K-strided).
+  auto read_slab = [&](int Q, bf16x8 (&af)[8]) __attribute__((always_inline)) {
+    const uint32_t m = (uint32_t)(2 * Q + (wave >> 1));
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
       uint32_t off[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const uint32_t d = (uint32_t)(16 * st + 8 * hh + 4 * r + (i16 >> 2));
-        const uint32_t q = (uint32_t)(4 * t + 2 * gm + ((i16 & 3) >> 1));
-        off[r] = ((uint32_t)wave * kNope + d) * 128u + ((q ^ (2u * (d & 3u))) * 16u) + 8u * (uint32_t)(i16 & 1);
+        const uint32_t q = (uint32_t)(4 * (wave & 1) + 2 * gm + ((i16 & 3) >> 1));
+        off[r] = (m * kNope + d) * 128u + ((q ^ (2u * (d & 3u))) * 16u) + 8u * (uint32_t)(i16 & 1);
       }
-      af[t][st] = tr_pair(wl + off[0], wl + off[1]);
+      af[st] = tr_pair(wl + off[0], wl + off[1]);
     }
-  // The slab is in registers now; its LDS holds output tiles from here on,
-  // two alternating 16 KB buffers: row r (batch row of the tile) = 512
-  // bytes, 16-byte chunk c stored at position c ^ (r % 32), so that the
-  // global writes are whole row segments.  One barrier per tile: a wave
-  // stages tile t + 1 into the buffer of tile t - 1 only after the barrier of
-  // tile t, which every wave reaches after its copy-out of tile t - 1.
-  __syncthreads();
+  };
+  // Output tile of quarter Q, batch tile bt (staged in the quarter-0 region
+  // once its fragments are in registers, two alternating 8 KB buffers): row r
+  // (batch row) = 256 bytes, 16-byte chunk c at position c ^ (r % 16).  One
+  // barrier per tile: a wave stages tile t + 1 into the buffer of tile t - 1
+  // only after the barrier of tile t, which every wave reaches after its
+  // copy-out of tile t - 1.
+  int ntile = 0;
+  auto out_tile = [&](int Q, int bt, const bf16x8 (&af)[8], const bf16x8 (&qb)[8]) __attribute__((always_inline)) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) acc = mfma32(af[st], qb[st], acc);
+    // acc[v]: batch row lane % 32, column 128 Q + 32 w + 8 (v / 4) + 4 hh + v % 4.
+    char* ot = wt + (ntile & 1) * 8192;
+    ++ntile;
+    char* orow = ot + (lane & 31) * 256 + 8 * hh;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c = 4 * wave + q4;
+      *reinterpret_cast<uint2*>(orow + ((c ^ (lane & 15)) << 4)) =
+          pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    }
+    __syncthreads();
+    // Thread t copies chunk t % 16 of rows t / 16 and t / 16 + 16.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = (tid >> 4) + 16 * k, c = tid & 15;
+      const int bb = bt * 32 + r;
+      const uint4 val = *reinterpret_cast<const uint4*>(ot + r * 256 + ((c ^ (r & 15)) << 4));
+      if (bb < a.B)
+        *reinterpret_cast<uint4*>(a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + 128 * Q + 8 * c) = val;
+    }
+  };
+
+  bf16x8 af0[8], af1[8];
+  bf16x8 qb[4][8];
   for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
-    if (bt0 > 0) load_q(bt0);
+    const int nq = min(4, nbt - bt0);
+    if (bt0 == 0) {
+      // Quarter 0 of the slab, the first query tiles, quarter 1 of the slab.
+      stage_slab(0);
+      stage_q(0);
+      stage_slab(1);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      // Every wave is done with the previous query tiles (their reads
+      // completed before its last copy-out, which precedes the barrier of
+      // its last output tile).
+      __syncthreads();
+      stage_q(bt0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (bt0 == 0) read_slab(0, af0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (bt0 + u >= nbt) break;
-      f32x16 acc[2] = {f32x16{}, f32x16{}};
+      if (u >= nq) break;
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma32(af[t][st], qb[u][st], acc[t]);
-      // acc[t][v]: batch row lane % 32, column 64 w + 32 t + 8 (v / 4) + 4 hh + v % 4.
-      char* ot = wt + ((bt0 + u) & 1) * 16384;
-      char* orow = ot + (lane & 31) * 512 + 8 * hh;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = 8 * wave + 4 * t + q4;
-          *reinterpret_cast<uint2*>(orow + ((c ^ (lane & 31)) << 4)) =
-              pack4(acc[t][4 * q4], acc[t][4 * q4 + 1], acc[t][4 * q4 + 2], acc[t][4 * q4 + 3]);
-        }
+      for (int st = 0; st < 8; ++st) qb[u][st] = *(const bf16x8 LDS_AS*)(wl + (qt0 - lds0) + u * kAbsQTile + qk_off(st));
+    }
+    if (bt0 == 0) {
+      // The quarter-0 region holds output tiles from here on.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __syncthreads();
-      // Thread t copies chunk t % 32 of rows t / 32 + 8 k.
+    }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = (tid >> 5) + 8 * k, c = tid & 31;
-        const int bb = (bt0 + u) * 32 + r;
-        const uint4 val = *reinterpret_cast<const uint4*>(ot + r * 512 + ((c ^ r) << 4));
-        if (bb < a.B)
-          *reinterpret_cast<uint4*>(a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + 8 * c) = val;
-      }
+    for (int u = 0; u < 4; ++u) {
+      if (u >= nq) break;
+      out_tile(0, bt0 + u, af0, qb[u]);
+    }
+    if (bt0 == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      read_slab(1, af1);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u >= nq) break;
+      out_tile(1, bt0 + u, af1, qb[u]);
     }
   }
 }

@@ -126,6 +126,7 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.mla_absorb_q(FAKE, 16384, 128, FAKE, FAKE, 0, None) == BADDIM
     assert lib.mla_absorb_q(FAKE + 4, 16384, 128, FAKE, FAKE, 1, None) == ALIGN
     assert lib.mla_absorb_q(FAKE, 16384, 127, FAKE, FAKE, 1, None) == ALIGN
+    assert lib.mla_absorb_q(FAKE, 1 << 28, 128, FAKE, FAKE, 9, None) == RANGE   # 32-bit row offsets
     assert lib.mla_value_up(FAKE, None, FAKE, 16384, 128, 1, None) == NULLP
     assert lib.mla_value_up(FAKE, FAKE, FAKE, 16384, 128, 70000, None) == BADDIM
     assert lib.mla_combine(None, 0, 4, 1, FAKE, None, None, None) == OK   # one split: no-op
