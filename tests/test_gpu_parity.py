@@ -30,6 +30,17 @@ def test_absorb_q(mla):
     assert rel_err(f64(q_abs), ref) <= 4e-3
 
 
+def test_absorb_q_many_batch_tiles(mla):
+    """B = 200: seven 32-row batch tiles, so the query rows are staged in two
+    groups of at most four tiles (the second after the first group's tiles
+    are written)."""
+    w = workload.make("sparse_b32_l4096_k2048", B=200, L=8, k=4)
+    g = to_gpu(w)
+    q_abs = mla.mla_absorb_q(g.q_nope, g.wkv_b)
+    torch.cuda.synchronize()
+    assert rel_err(f64(q_abs), oracle.absorb(w.q_nope, w.wkv_b)) <= 4e-3
+
+
 def test_absorb_q_strided_query(mla):
     """q_nope as the first 128 columns of a [B,1,128,192] query tensor."""
     B = 5
@@ -76,6 +87,8 @@ CASES = [
     ("longctx_b64_k2048", 4, 3000, 700, 5, "packed"),
     ("dense_p1000_b1", 2, 1001, None, 1, "packed"),
     ("dense_p1000_b1", 2, 1001, None, 4, "split"),
+    ("sparse_b32_l4096_k2048", 5, 300, 101, 2, "packed"),   # odd slot count: per-slot range checks
+    ("sparse_b32_l4096_k2048", 300, 120, 40, 1, "packed"),  # more workgroups than CUs
 ]
 
 
@@ -102,6 +115,21 @@ def test_decode_small(mla, case):
         assert rel_err(f64(out2)[:, 0], ref["out"]) <= REL_TOL
         assert np.all(lse_dev(f64(bufs2.lse), ref) <= tol)
         assert rowsum_dev(f64(scores), f64(bufs2.lse)) <= ROWSUM_TOL
+
+
+def test_decode_strided_q_pe(mla):
+    """q_pe as the last 64 columns of a [B,1,128,192] query tensor (head
+    stride 192): the query tile staging reads it through its strides."""
+    w = workload.make("longctx_b64_k2048", B=3, L=3000, k=300)
+    g = to_gpu(w)
+    q = torch.zeros((w.B, 1, 128, 192), dtype=torch.bfloat16, device="cuda")
+    q[..., 128:] = g.q_pe
+    g.q_pe = q[..., 128:]
+    assert g.q_pe.stride(2) == 192
+    for S in (1, 2):
+        bufs, out = _run_decode(mla, g, S)
+        ref = oracle_ref(w)
+        assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
 
 
 def test_decode_validate_bitmap_and_scores(mla):
