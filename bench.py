@@ -11,9 +11,10 @@ cannot serve a repeated step.  Prints ONE JSON line.
 
 The roofline entry is for the dominant kernel (the sparse decode): its
 algorithmic bytes per launch (selected cache rows at 1152 B + 4 B per index)
-over its mean launch time, timed with HIP events around each decode launch on
-its stream in a second pass over the same steps (the throughput pass has no
-events inside the steps).
+over its mean launch time, from HIP events bracketing K decode launches
+issued back to back on its stream over the same rotating input sets (their
+absorbed queries computed beforehand; the throughput pass has no events
+inside the steps, and an event pair around every launch would add ~3 us).
 The CPU baseline runs the fp64 oracle (oracle/, test infrastructure) on a
 bounded sample of the same workload.
 
@@ -195,15 +196,11 @@ def main():
     bufs = mla.DecodeBuffers.allocate(B, k_max, dense, num_splits=args.splits)
     stream = torch.cuda.current_stream()
 
-    def step(w, ev=None):
+    def step(w):
         mla.mla_absorb_q(w.q_nope, w.wkv_b, bufs.q_abs)
-        if ev is not None:
-            ev[0].record(stream)
         mla.mla_sparse_decode(bufs.q_abs, w.q_pe, w.kv, w.pe, w.seq_lens, w.max_len, w.indices, w.scale,
                               bufs.num_splits, bufs.workspace, bufs.o_latent, bufs.lse,
                               k_max=k_max)
-        if ev is not None:
-            ev[1].record(stream)
         if bufs.num_splits > 1:
             mla.mla_combine_value_up(bufs.workspace, B, bufs.num_splits, w.wkv_b, bufs.out, lse=bufs.lse)
         else:
@@ -226,13 +223,27 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    # Pass 2 (kernel time for the roofline): the same K steps again, with HIP
-    # events bracketing each decode launch on its stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Pass 2 (kernel time for the roofline): K decode launches back to back on
+    # the same stream, cycling the input sets (their absorbed queries computed
+    # beforehand), bracketed by two HIP events.  An event pair around every
+    # launch would add ~3 us to each; back to back, the mean includes the
+    # short gap between consecutive launches and nothing else.
+    qabs = [mla.mla_absorb_q(w.q_nope, w.wkv_b) for w in sets]
+
+    def decode_only(i):
+        w = sets[i % R]
+        mla.mla_sparse_decode(qabs[i % R], w.q_pe, w.kv, w.pe, w.seq_lens, w.max_len, w.indices, w.scale,
+                              bufs.num_splits, bufs.workspace, bufs.o_latent, bufs.lse, k_max=k_max)
+
+    for i in range(min(args.warmup, 100)):
+        decode_only(i)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
     for i in range(args.steps):
-        step(sets[i % R], evs[i])
+        decode_only(i)
+    d1.record(stream)
     torch.cuda.synchronize()
-    decode_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    decode_ms = d0.elapsed_time(d1) / args.steps
     log(f"{args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us), "
         f"decode kernel {decode_ms * 1e3:.2f} us; plan splits={bufs.num_splits}")
 
