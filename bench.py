@@ -15,6 +15,9 @@ over its mean launch time, from HIP events bracketing K decode launches
 issued back to back on its stream over the same rotating input sets (their
 absorbed queries computed beforehand; the throughput pass has no events
 inside the steps, and an event pair around every launch would add ~3 us).
+The line also carries the per-head-query rate (128 x queries/s) and the
+attention-only rate: B over the mean time of decode + the separate split
+combine, K pairs back to back (value-up excluded).
 The CPU baseline runs the fp64 oracle (oracle/, test infrastructure) on a
 bounded sample of the same workload.
 
@@ -38,6 +41,7 @@ FLOP_PER_KEY = 2 * 128 * (576 + 512)
 WEIGHT_BYTES = 2 * 128 * 128 * 512 * 2   # W_UK and W_UV, bf16
 Q_BYTES_PER_QUERY = 128 * (128 + 64) * 2
 O_BYTES_PER_QUERY = 128 * 128 * 2
+HEADS = 128                    # query heads; one query = one sequence across all heads
 METRIC = "sparse MLA decode queries/s at B=64,k=2048; % of HBM/MFMA roofline"
 ROTATION = {"dense_p1000_b1": 32, "sparse_b32_l4096_k2048": 10, "longctx_b64_k2048": 6,
             "verylong_b128_l131072_k2048": 3, "dense_fp8w_b64_l8192": 2}
@@ -244,8 +248,25 @@ def main():
     d1.record(stream)
     torch.cuda.synchronize()
     decode_ms = d0.elapsed_time(d1) / args.steps
+    # Pass 3 (attention-only rate): the key splits' decode plus the separate
+    # split combine that yields the normalised latent output and its LSE, K
+    # pairs back to back; value-up is left out.
+    def attention_only(i):
+        decode_only(i)
+        if bufs.num_splits > 1:
+            mla.mla_combine(bufs.workspace, B, bufs.num_splits, bufs.o_latent, lse=bufs.lse)
+
+    for i in range(min(args.warmup, 100)):
+        attention_only(i)
+    d0.record(stream)
+    for i in range(args.steps):
+        attention_only(i)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = d0.elapsed_time(d1) / args.steps
     log(f"{args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us), "
-        f"decode kernel {decode_ms * 1e3:.2f} us; plan splits={bufs.num_splits}")
+        f"decode kernel {decode_ms * 1e3:.2f} us, decode + combine {attn_ms * 1e3:.2f} us; "
+        f"plan splits={bufs.num_splits}")
 
     # Algorithmic work.
     if dense:
@@ -320,6 +341,10 @@ def main():
             "mfma_frac": dec_tflops / BF16_PEAK_TFLOPS,
         },
         "step_roofline_frac": step_roof_s / (ms_step * 1e-3),
+        "head_queries_per_s": HEADS * B / (ms_step * 1e-3),
+        "attention_only": {"value": B / (attn_ms * 1e-3), "unit": "queries/s", "us": attn_ms * 1e3,
+                           "kernels": "mla_sparse_decode + mla_combine" if bufs.num_splits > 1
+                           else "mla_sparse_decode"},
         "parity_sampled_rel_err": parity,
         "cpu_baseline": cpu,
     }
