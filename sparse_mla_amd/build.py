@@ -1,4 +1,5 @@
-"""Build libmla_decode.so (HIP for gfx950) in-tree with hipcc.
+"""Build libmla_decode.so (the decode path) and libmla_peaks.so (the
+attainable-peak microbenchmarks) for gfx950, in-tree, with hipcc.
 
     python -m sparse_mla_amd.build
 """
@@ -12,6 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = [os.path.join(HERE, "csrc", "mla_kernels.hip"), os.path.join(HERE, "csrc", "mla_api.cpp")]
+PEAKS_LIB = os.path.join(HERE, "libmla_peaks.so")
+PEAKS_SOURCES = [os.path.join(HERE, "csrc", "mla_peaks.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -32,8 +35,14 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    _compile(SOURCES, LIB, verbose)
+    _compile(PEAKS_SOURCES, PEAKS_LIB, verbose)
+    return LIB
+
+
+def _compile(sources, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,8 +52,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

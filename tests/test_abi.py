@@ -136,3 +136,47 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.mla_combine_value_up(FAKE, 10, 4, 2, FAKE, FAKE, 16384, 128, None, None, None) == WS
     assert lib.mla_dequant_wkv_b_fp8(None, FAKE, FAKE, None) == NULLP
     assert lib.mla_dequant_wkv_b_fp8(FAKE + 2, FAKE, FAKE, None) == ALIGN
+
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "mla_peaks.h")
+PEAKS_LIB = os.path.join(ROOT, "sparse_mla_amd", "libmla_peaks.so")
+
+
+@pytest.fixture(scope="module")
+def peaks():
+    if not os.path.exists(PEAKS_LIB):
+        from sparse_mla_amd import build
+        build.build()
+    L = ctypes.CDLL(PEAKS_LIB)
+    p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.mlap_stream_read.argtypes = [p, sz, i32, p, p]
+    L.mlap_row_gather.argtypes = [p, sz, p, i32, i32, p, p]
+    L.mlap_mfma_bf16.argtypes = [i32, i32, p, p]
+    return L
+
+
+def test_peaks_exports_every_declared_symbol(peaks):
+    text = re.sub(r"/\*.*?\*/", "", open(PEAKS_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(mlap_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["mlap_mfma_bf16", "mlap_row_gather", "mlap_stream_read"]
+    for n in names:
+        assert hasattr(peaks, n), f"{n} declared in include/mla_peaks.h but not exported"
+
+
+def test_peaks_reject_bad_arguments(peaks):
+    # Return 1 (argument rejected) before any launch: fake, aligned addresses
+    # are never dereferenced on these paths.
+    a = 1 << 20
+    assert peaks.mlap_stream_read(None, 1024, 4, a, None) == 1
+    assert peaks.mlap_stream_read(a, 0, 4, a, None) == 1
+    assert peaks.mlap_stream_read(a, 1000, 4, a, None) == 1      # not a multiple of 16
+    assert peaks.mlap_stream_read(a + 8, 1024, 4, a, None) == 1  # misaligned
+    assert peaks.mlap_stream_read(a, 1024, 0, a, None) == 1
+    assert peaks.mlap_row_gather(a, 1 << 20, a, 4, 48, a, None) == 1      # not a multiple of 32
+    assert peaks.mlap_row_gather(a, 1 << 20, a, 4, 2048, a, None) == 1    # above 1024
+    assert peaks.mlap_row_gather(a, 1 << 33, a, 4, 512, a, None) == 1     # beyond 32-bit offsets
+    assert peaks.mlap_row_gather(a, 1 << 20, None, 4, 512, a, None) == 1
+    assert peaks.mlap_row_gather(a, 1 << 20, a, 0, 512, a, None) == 1
+    assert peaks.mlap_mfma_bf16(0, 10, a, None) == 1
+    assert peaks.mlap_mfma_bf16(4, 0, a, None) == 1
+    assert peaks.mlap_mfma_bf16(4, 10, None, None) == 1
