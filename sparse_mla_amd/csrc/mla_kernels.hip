@@ -1116,10 +1116,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int col = (threadIdx.x & 127) * 4;
   const int64_t stride_s = (int64_t)a.B * kHeads;
   const int64_t bh = (int64_t)b * kHeads + head;
+  // Unrolled so that the loads of several splits are in flight together
+  // (one at a time, a 32-split merge is 32 memory latencies long).
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[(s * stride_s + bh) * 2]);
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
   for (int s = 0; s < a.S; ++s) {
     const float ms = a.part_ml[(s * stride_s + bh) * 2];
     const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
