@@ -1109,30 +1109,51 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 // combine: O~ = sum_s g_s U_s, g_s = 2^(m_s - M) / L, L = sum_s 2^(m_s - M) l_s,
 // where U_s is split s's unnormalised sum (relative to its max m_s).
 // Workgroup = (sequence, 2 heads); each thread owns 4 latent columns.
+// G = splits per group (2, 4 or 8, the smallest >= S up to 8).
 // ---------------------------------------------------------------------------
+template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
   const int b = blockIdx.x >> 6;
   const int head = (blockIdx.x & 63) * 2 + (threadIdx.x >> 7);
   const int col = (threadIdx.x & 127) * 4;
   const int64_t stride_s = (int64_t)a.B * kHeads;
   const int64_t bh = (int64_t)b * kHeads + head;
-  // Unrolled so that the loads of several splits are in flight together
-  // (one at a time, a 32-split merge is 32 memory latencies long).
+  // Splits in groups of G whose loads are all in flight together (one at a
+  // time, a 32-split merge is 32 memory latencies long); a group's slots past
+  // S re-read split S - 1 (in bounds) and get weight 0.  The sums run over
+  // s = 0 .. S - 1 in order.
   float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < a.S; ++s) M = fmaxf(M, a.part_ml[(s * stride_s + bh) * 2]);
+  for (int s0 = 0; s0 < a.S; s0 += G) {
+    float mv[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) mv[u] = a.part_ml[(min(s0 + u, a.S - 1) * stride_s + bh) * 2];
+#pragma unroll
+    for (int u = 0; u < G; ++u) M = fmaxf(M, mv[u]);
+  }
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < a.S; ++s) {
-    const float ms = a.part_ml[(s * stride_s + bh) * 2];
-    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    L += w * a.part_ml[(s * stride_s + bh) * 2 + 1];
-    const uint2 v = *reinterpret_cast<const uint2*>(a.part_o + (s * stride_s + bh) * kLatent + col);
-    acc[0] += w * __uint_as_float(v.x << 16);
-    acc[1] += w * __uint_as_float(v.x & 0xffff0000u);
-    acc[2] += w * __uint_as_float(v.y << 16);
-    acc[3] += w * __uint_as_float(v.y & 0xffff0000u);
+  for (int s0 = 0; s0 < a.S; s0 += G) {
+    float2 ml[G];
+    uint2 v[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int64_t row = min(s0 + u, a.S - 1) * stride_s + bh;
+      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+      v[u] = *reinterpret_cast<const uint2*>(a.part_o + row * kLatent + col);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      // Weight 0 for the unused slots (a select, not a branch, so that the
+      // loads above stay ahead of all the arithmetic): their finite terms add
+      // nothing.
+      const bool used = s0 + u < a.S && ml[u].x != -INFINITY;
+      const float w = used ? __builtin_amdgcn_exp2f(ml[u].x - M) : 0.f;
+      L += w * ml[u].y;
+      acc[0] += w * __uint_as_float(v[u].x << 16);
+      acc[1] += w * __uint_as_float(v[u].x & 0xffff0000u);
+      acc[2] += w * __uint_as_float(v[u].y << 16);
+      acc[3] += w * __uint_as_float(v[u].y & 0xffff0000u);
+    }
   }
   const float inv = 1.0f / L;
   *reinterpret_cast<uint2*>(a.o_latent + bh * kLatent + col) =
@@ -1212,7 +1233,9 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 }
 
 int launch_combine(const CombineArgs& a, void* stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
+  if (a.S <= 2) hipLaunchKernelGGL(combine_kernel<2>, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
+  else if (a.S <= 4) hipLaunchKernelGGL(combine_kernel<4>, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
+  else hipLaunchKernelGGL(combine_kernel<8>, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
