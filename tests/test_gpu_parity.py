@@ -89,6 +89,8 @@ CASES = [
     ("dense_p1000_b1", 2, 1001, None, 4, "split"),
     ("sparse_b32_l4096_k2048", 5, 300, 101, 2, "packed"),   # odd slot count: per-slot range checks
     ("sparse_b32_l4096_k2048", 300, 120, 40, 1, "packed"),  # more workgroups than CUs
+    ("dense_p1000_b1", 1, 1001, None, 32, "packed"),          # one row, 32 splits in one value-up pass
+    ("dense_p1000_b1", 3, 1001, None, 24, "split"),           # 3 rows, 24 splits (8 empty), two passes
 ]
 
 
