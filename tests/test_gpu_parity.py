@@ -91,6 +91,8 @@ CASES = [
     ("sparse_b32_l4096_k2048", 300, 120, 40, 1, "packed"),  # more workgroups than CUs
     ("dense_p1000_b1", 1, 1001, None, 32, "packed"),          # one row, 32 splits in one value-up pass
     ("dense_p1000_b1", 3, 1001, None, 24, "split"),           # 3 rows, 24 splits (8 empty), two passes
+    ("sparse_b32_l4096_k2048", 2, 4096, 2048, 64, "packed"),  # the most splits: one block each
+    ("sparse_b32_l4096_k2048", 33, 300, 100, 2, "packed"),    # 32-row value-up tiles, a 1-row tile
 ]
 
 
