@@ -22,6 +22,7 @@ from .core import (  # noqa: F401
     decode,
     absorb,
     value_up,
+    output_proj,
     dequant_fp8,
     e4m3_to_double,
     bf16_bits_to_double,

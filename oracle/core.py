@@ -66,6 +66,8 @@ def load(path: str | None = None):
         lib.oracle_absorb.argtypes = [i64, i64, i64, i64, i64, p, p, p]
         lib.oracle_value_up.restype = ctypes.c_int
         lib.oracle_value_up.argtypes = [i64, i64, i64, i64, i64, p, p, p]
+        lib.oracle_output_proj.restype = ctypes.c_int
+        lib.oracle_output_proj.argtypes = [i64, i64, i64, p, p, p]
         if path is not None:
             return lib
         _lib = lib
@@ -196,6 +198,23 @@ def value_up(o_lat, wkv_b, Dn=128, lib=None):
     out = np.empty((B, H, Dv))
     if lib.oracle_value_up(B, H, Dn, Dc, Dv, _ptr(o), _ptr(w), _ptr(out)):
         raise ValueError("oracle_value_up: bad arguments")
+    return out
+
+
+def output_proj(x, wo, lib=None):
+    """Output projection alone: out [B, Dout] from the head outputs x
+    ([B, Din], or [B, 1, H, Dv] flattened per sequence) and wo [Dout, Din]."""
+    lib = lib or load()
+    a = _f64(x)
+    a = np.ascontiguousarray(a.reshape(a.shape[0], -1))
+    w = np.ascontiguousarray(_f64(wo))
+    B, Din = a.shape
+    Dout = w.shape[0]
+    if w.shape[1] != Din:
+        raise ValueError("wo must be [Dout, Din] with Din = the flattened head outputs")
+    out = np.empty((B, Dout))
+    if lib.oracle_output_proj(B, Din, Dout, _ptr(a), _ptr(w), _ptr(out)):
+        raise ValueError("oracle_output_proj: bad arguments")
     return out
 
 

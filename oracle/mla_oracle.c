@@ -303,3 +303,20 @@ int oracle_value_up(int64_t B, int64_t H, int64_t Dn, int64_t Dc, int64_t Dv,
     }
     return ORACLE_OK;
 }
+
+/* Output projection ("Attention update" page, mla-output excerpt): each
+ * sequence's head outputs flattened to one vector x[b][i] (i = h * Dv + d)
+ * and projected to the model width by the output linear layer:
+ * out[b][o] = sum_i x[b][i] * wo[o][i], with wo stored [Dout][Din] as a
+ * linear layer's weight (no bias). */
+int oracle_output_proj(int64_t B, int64_t Din, int64_t Dout, const double* x, const double* wo, double* out) {
+    if (B <= 0 || Din <= 0 || Dout <= 0 || !x || !wo || !out) return ORACLE_ERR_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t bo = 0; bo < B * Dout; ++bo) {
+        const int64_t b = bo / Dout, o = bo % Dout;
+        double acc = 0.0;
+        for (int64_t i = 0; i < Din; ++i) acc += x[b * Din + i] * wo[o * Din + i];
+        out[bo] = acc;
+    }
+    return ORACLE_OK;
+}

@@ -56,3 +56,20 @@ def test_mutant_fails_a_pin(tmp_path, name):
         except (AssertionError, IndexError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+OUTPUT_PROJ_MUTANTS = {
+    "transpose_wo": ("x[b * Din + i] * wo[o * Din + i]", "x[b * Din + i] * wo[i * Dout + o]"),
+    "wo_drops_last_input": ("for (int64_t i = 0; i < Din; ++i) acc += x[b * Din + i]",
+                            "for (int64_t i = 0; i + 1 < Din; ++i) acc += x[b * Din + i]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(OUTPUT_PROJ_MUTANTS))
+def test_output_proj_mutant_fails_the_pin(tmp_path, name, monkeypatch):
+    from tests import test_oracle_pins as tp
+    lib = _build_mutant(tmp_path, name, *OUTPUT_PROJ_MUTANTS[name])
+    real = oracle.output_proj
+    monkeypatch.setattr(oracle, "output_proj", lambda x, wo: real(x, wo, lib=lib))
+    with pytest.raises(AssertionError):
+        tp.test_output_proj_brute_force()

@@ -135,3 +135,40 @@ def test_step_value_up_identity_and_agreement():
     w[:, Dn + np.arange(Dv), np.arange(Dv)] = 1.0
     o = np.random.default_rng(1).standard_normal((2, H, Dc))
     assert np.array_equal(oracle.value_up(o, w.reshape(-1, Dc)), o[:, :, :Dv])
+
+
+def _exact_output_proj(x, wo):
+    """Brute force with exact rational arithmetic (Python fractions): each
+    sum of products written out, then rounded once to float."""
+    from fractions import Fraction
+    B, Din = x.shape
+    Dout = wo.shape[0]
+    out = np.empty((B, Dout))
+    for b in range(B):
+        for o in range(Dout):
+            out[b, o] = float(sum(Fraction(float(x[b, i])) * Fraction(float(wo[o, i])) for i in range(Din)))
+    return out
+
+
+def test_output_proj_brute_force():
+    # "Attention update" page, mla-output: out[b][o] = sum_i x[b][i] wo[o][i]
+    # on non-square shapes (a transposed operand or a dropped term fails).
+    g = torch.Generator().manual_seed(607)
+    for B, Din, Dout in [(2, 6, 3), (3, 5, 7), (1, 16, 2)]:
+        x = torch.randn(B, Din, generator=g).to(torch.bfloat16)
+        wo = torch.randn(Dout, Din, generator=g).to(torch.bfloat16)
+        got = oracle.output_proj(x, wo)
+        ref = _exact_output_proj(x.double().numpy(), wo.double().numpy())
+        assert np.max(np.abs(got - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_output_proj_selection_at_the_real_shape():
+    # One 1 per row of wo: out[b][o] = x[b][perm(o)] exactly, with x the
+    # flattened [B, 1, 128, 128] head outputs and the model width 7168.
+    g = torch.Generator().manual_seed(608)
+    x = torch.randn(2, 1, 128, 128, generator=g).to(torch.bfloat16)
+    perm = torch.randperm(128 * 128, generator=g)[:7168]
+    wo = torch.zeros(7168, 128 * 128, dtype=torch.bfloat16)
+    wo[torch.arange(7168), perm] = 1
+    got = oracle.output_proj(x, wo)
+    assert np.array_equal(got, x.reshape(2, -1).double().numpy()[:, perm.numpy()])
