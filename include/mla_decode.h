@@ -206,6 +206,24 @@ int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int3
  */
 int mla_dequant_wkv_b_fp8(const void* w_fp8, const float* scales, void* w_bf16, void* stream);
 
+/*
+ * Output projection, the step after the value-up ("Attention update" page,
+ * mla-output excerpt: the head outputs are flattened per sequence and the
+ * output linear layer maps them to the model width):
+ *   out[b][o] = sum_i x[b][i] * wo[o][i],  i < 16384 = 128 heads x 128, o < 7168.
+ *   x    bf16 [B][x_sb]: row b's first 16384 values are head h's 128 outputs
+ *        at 128 h .. (the [B][1][128][128] value-up output, contiguous, has
+ *        x_sb = 16384); x_sb >= 16384, a multiple of 8; 16-byte aligned.
+ *   wo   bf16 [7168][16384], contiguous (a linear layer's weight), 16-byte aligned.
+ *   out  bf16 [B][out_sb], out_sb >= 7168: the first 7168 values of each row
+ *        are written; 2-byte aligned.
+ * fp32 accumulation, one rounding to bf16.  Launches one kernel per 64 rows
+ * of the batch.  Errors: MLA_ERR_NULL_POINTER, MLA_ERR_BAD_DIM (B outside
+ * 1 .. 65536, a row stride below the row width), MLA_ERR_ALIGNMENT, MLA_ERR_HIP.
+ */
+int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

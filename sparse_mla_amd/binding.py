@@ -62,6 +62,8 @@ _value_up = _sig("mla_value_up", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p
 _combine_value_up = _sig("mla_combine_value_up", ctypes.c_int,
                          [_p, _sz, _i32, _i32, _p, _p, _i64, _i64, _p, _p, _p])
 _dequant = _sig("mla_dequant_wkv_b_fp8", ctypes.c_int, [_p, _p, _p, _p])
+_output_proj = _sig("mla_output_proj", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p])
+MODEL_DIM = 7168
 
 
 class MLAError(RuntimeError):
@@ -218,6 +220,30 @@ def mla_combine_value_up(workspace, B: int, num_splits: int, wkv_b: torch.Tensor
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("mla_combine_value_up", _combine_value_up(_ptr(workspace), ws_bytes, B, num_splits, _ptr(wkv_b),
                                                      _ptr(out), sb, sh, _ptr(lse), _ptr(status), _stream(stream)))
+    return out
+
+
+def mla_output_proj(x: torch.Tensor, wo: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """x: the value-up output, bf16 [B, 1, 128, 128] or [B, 16384] (each row's
+    16384 values contiguous); wo: bf16 [7168, 16384], contiguous.  Returns
+    out bf16 [B, 1, 7168] (or writes `out`, [B, 1, 7168] or [B, 7168])."""
+    _need(x, "x", torch.bfloat16)
+    _need(wo, "wo", torch.bfloat16, 2)
+    B = x.shape[0]
+    xf = x.reshape(B, -1)
+    if xf.shape[1] != HEADS * VALUE or xf.stride(1) != 1 or xf.data_ptr() != x.data_ptr():
+        raise ValueError("x must hold 16384 contiguous values per sequence")
+    if tuple(wo.shape) != (MODEL_DIM, HEADS * VALUE) or not wo.is_contiguous():
+        raise ValueError("wo must be a contiguous [7168, 16384] tensor")
+    if out is None:
+        out = torch.empty((B, 1, MODEL_DIM), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16)
+    of = out.reshape(B, -1)
+    if of.shape[1] != MODEL_DIM or of.stride(1) != 1 or of.data_ptr() != out.data_ptr():
+        raise ValueError("out must be [B, 1, 7168] or [B, 7168] with contiguous rows")
+    _check("mla_output_proj", _output_proj(_ptr(x), xf.stride(0), _ptr(wo), _ptr(out), of.stride(0), B,
+                                           _stream(stream)))
     return out
 
 

@@ -220,6 +220,26 @@ int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
   return hip_status(mla::launch_value_up(a, stream));
 }
 
+int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
+                    void* stream) {
+  if (!x || !wo || !out) return MLA_ERR_NULL_POINTER;
+  if (B < 1 || B > 65536 || x_sb < mla::kWoIn || out_sb < mla::kWoOut) return MLA_ERR_BAD_DIM;
+  if (!aligned16(x) || !aligned16(wo) || !stride8(x_sb) || (reinterpret_cast<uintptr_t>(out) & 1u) != 0)
+    return MLA_ERR_ALIGNMENT;
+  for (int32_t b0 = 0; b0 < B; b0 += 64) {
+    mla::OutProjArgs a;
+    a.x = static_cast<const uint16_t*>(x) + (int64_t)b0 * x_sb;
+    a.wo = static_cast<const uint16_t*>(wo);
+    a.out = static_cast<uint16_t*>(out) + (int64_t)b0 * out_sb;
+    a.x_sb = x_sb;
+    a.out_sb = out_sb;
+    a.B = B - b0 < 64 ? B - b0 : 64;
+    const int st = hip_status(mla::launch_output_proj(a, stream));
+    if (st != MLA_OK) return st;
+  }
+  return MLA_OK;
+}
+
 int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
                          const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh, float* lse,
                          uint32_t* status_dev, void* stream) {

@@ -80,12 +80,24 @@ struct DequantArgs {
   uint16_t* out;
 };
 
+// Output projection: out[b][o] = sum_i x[b][i] wo[o][i], at most 64 rows.
+constexpr int kWoIn = kHeads * kValue;  // 16384: the head outputs flattened
+constexpr int kWoOut = 7168;            // model width
+struct OutProjArgs {
+  const uint16_t* x;    // [B][x_sb], the first kWoIn values of each row used
+  const uint16_t* wo;   // [kWoOut][kWoIn]
+  uint16_t* out;        // [B][out_sb], the first kWoOut values of each row written
+  int64_t x_sb, out_sb;
+  int32_t B;            // 1 .. 64
+};
+
 // Each returns a hipError_t value (0 on success).
 int launch_absorb(const AbsorbArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_combine(const CombineArgs& a, void* stream);
 int launch_value_up(const ValueUpArgs& a, void* stream);  // fused combine when o_latent == NULL
 int launch_dequant(const DequantArgs& a, void* stream);
+int launch_output_proj(const OutProjArgs& a, void* stream);
 int device_cu_count(int* cus);
 
 }  // namespace mla

@@ -1165,6 +1165,78 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// output projection ("Attention update" page, mla-output): each sequence's
+// head outputs flattened (i = 128 h + d) and projected to the model width,
+//   out[b][o] = sum_i x[b][i] wo[o][i],  wo [7168][16384] (a linear weight).
+// HBM-bound on wo (235 MB): each weight is read once per launch of up to 64
+// batch rows.  Workgroup = 32 output features (224 workgroups); wave w sums
+// over inputs 4096 w .. 4096 w + 4095 (256 steps of 16) and the four partial
+// sums are added through LDS.  M = o (wo rows, 16-byte loads straight into the
+// MFMA A layout: lane l takes row l % 32, inputs 8 (l / 32) .. + 7 of the
+// step), N = b (x rows, B layout, rows past B repeat row B - 1 and are not
+// stored), K = i.  The loads of step group g (U = 4 steps) are issued D = 4
+// groups ahead into register rings, in the order they are needed, so the
+// in-order wait for group g never covers a later group.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a) {
+  constexpr int U = 4, D = 4, G = (kWoIn / 4) / (16 * U);  // 64 groups per wave
+  __shared__ float red[4][NT][64][16];
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = 32 * (int)blockIdx.x;
+  const int k0 = (kWoIn / 4) * wave + 8 * hh;
+  const uint16_t* pa = a.wo + (size_t)(n0 + r) * kWoIn + k0;
+  const uint16_t* pb[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) pb[t] = a.x + (int64_t)min(32 * t + r, a.B - 1) * a.x_sb + k0;
+  bf16x8 ra[D][U], rb[D][U][NT];
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  auto load = [&](int g, int d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ra[d][u] = ld8(pa + 16 * (U * g + u));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) rb[d][u][t] = ld8(pb[t] + 16 * (U * g + u));
+    }
+  };
+  auto mma = [&](int d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mfma32(ra[d][u], rb[d][u][t], acc[t]);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, d);
+  for (int g0 = 0; g0 < G - D; g0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      mma(d);
+      load(g0 + D + d, d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) mma(d);
+
+  // acc[t][v] of lane l: output feature n0 + 8 (v / 4) + 4 (l / 32) + v % 4,
+  // batch row 32 t + l % 32.
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave][t][lane][v] = acc[t][v];
+  __syncthreads();
+  for (int e = tid; e < NT * 64 * 16; e += 256) {
+    const int t = e >> 10, l = (e >> 4) & 63, v = e & 15;
+    const float sum = red[0][t][l][v] + red[1][t][l][v] + red[2][t][l][v] + red[3][t][l][v];
+    const int b = 32 * t + (l & 31);
+    if (b < a.B)
+      a.out[(int64_t)b * a.out_sb + n0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = __builtin_bit_cast(uint16_t, (__bf16)sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp8 dequantisation (one-time set-up).  E4M3FN from its definition: sign,
 // 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal
 // (m/8 * 2^-6); 0x7F / 0xFF are NaN.  The product with the fp32 block scale
@@ -1229,6 +1301,13 @@ int launch_decode(const DecodeArgs& a, void* stream) {
   auto* k = a.indices == nullptr ? (a.S > 1 ? decode_kernel<true, true> : decode_kernel<true, false>)
                                   : (a.S > 1 ? decode_kernel<false, true> : decode_kernel<false, false>);
   hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+int launch_output_proj(const OutProjArgs& a, void* stream) {
+  const dim3 grid(kWoOut / 32);
+  if (a.B <= 32) hipLaunchKernelGGL(output_proj_kernel<1>, grid, dim3(256), 0, (hipStream_t)stream, a);
+  else hipLaunchKernelGGL(output_proj_kernel<2>, grid, dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

@@ -195,3 +195,12 @@ def make(name_or_spec, device="cpu", B: Optional[int] = None, L: Optional[int] =
     return Workload(spec=spec, B=B, seq_lens=lens.to(device), max_len=max_len,
                     q_nope=q_nope, q_pe=q_pe, cache=cache, wkv_b=wkv_b, indices=idx,
                     wkv_b_fp8=codes, wkv_b_scale=sc)
+
+
+def output_proj_inputs(B: int, seed: int = 607, device="cpu"):
+    """Inputs of the output projection: head outputs x [B, 1, 128, 128] ~ N(0, 1)
+    and the output weight wo [7168, 128 * 128] ~ N(0, 1/16384) (variance
+    1/fan_in), bf16, drawn from generators seeded seed and seed + 1."""
+    x = _normal_bf16((B, 1, H, DV), _gen(device, seed), device)
+    wo = _normal_bf16((7168, H * DV), _gen(device, seed + 1), device, std=(H * DV) ** -0.5)
+    return x, wo

@@ -29,6 +29,7 @@ def lib():
     L.mla_combine.argtypes = [p, sz, i32, i32, p, p, p, p]
     L.mla_combine_value_up.argtypes = [p, sz, i32, i32, p, p, i64, i64, p, p, p]
     L.mla_dequant_wkv_b_fp8.argtypes = [p, p, p, p]
+    L.mla_output_proj.argtypes = [p, i64, p, p, i64, i32, p]
     L.mla_workspace_bytes.restype = sz
     L.mla_workspace_bytes.argtypes = [i32, i32]
     L.mla_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
@@ -180,3 +181,17 @@ def test_peaks_reject_bad_arguments(peaks):
     assert peaks.mlap_mfma_bf16(0, 10, a, None) == 1
     assert peaks.mlap_mfma_bf16(4, 0, a, None) == 1
     assert peaks.mlap_mfma_bf16(4, 10, None, None) == 1
+
+
+def test_output_proj_host_checks(lib):
+    a = 1 << 20  # fake aligned addresses: never dereferenced on these paths
+    assert lib.mla_output_proj(None, 16384, a, a, 7168, 4, None) == NULLP
+    assert lib.mla_output_proj(a, 16384, None, a, 7168, 4, None) == NULLP
+    assert lib.mla_output_proj(a, 16384, a, a, 7168, 0, None) == BADDIM
+    assert lib.mla_output_proj(a, 16384, a, a, 7168, 65537, None) == BADDIM
+    assert lib.mla_output_proj(a, 16376, a, a, 7168, 4, None) == BADDIM    # rows would overlap
+    assert lib.mla_output_proj(a, 16384, a, a, 7000, 4, None) == BADDIM
+    assert lib.mla_output_proj(a + 8, 16384, a, a, 7168, 4, None) == ALIGN
+    assert lib.mla_output_proj(a, 16388, a, a, 7168, 4, None) == ALIGN     # stride not a multiple of 8
+    assert lib.mla_output_proj(a, 16384, a + 8, a, 7168, 4, None) == ALIGN
+    assert lib.mla_output_proj(a, 16384, a, a + 1, 7168, 4, None) == ALIGN
