@@ -89,6 +89,7 @@ def parse():
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak microbenchmarks")
+    ap.add_argument("--no-output-proj", action="store_true", help="skip timing the output projection")
     ap.add_argument("--cpu-sample", type=int, default=None, help="sequences in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
@@ -289,6 +290,30 @@ def main():
     d1.record(stream)
     torch.cuda.synchronize()
     attn_ms = d0.elapsed_time(d1) / args.steps
+    # The step after the path, timed on its own (not part of `value`): the
+    # output projection of the B value-up outputs to the model width, K
+    # launches back to back over three weight copies (705 MB, beyond the
+    # memory-side cache), bracketed by two events.
+    oproj = None
+    if not args.no_output_proj:
+        ox, _ = workload.output_proj_inputs(B, device="cuda")
+        wos = [workload.output_proj_inputs(1, seed=700 + 2 * c, device="cuda")[1] for c in range(3)]
+        oout = torch.empty((B, 1, mla.MODEL_DIM), dtype=torch.bfloat16, device="cuda")
+        for i in range(6):
+            mla.mla_output_proj(ox, wos[i % 3], oout)
+        d0.record(stream)
+        for i in range(args.steps):
+            mla.mla_output_proj(ox, wos[i % 3], oout)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        op_ms = d0.elapsed_time(d1) / args.steps
+        op_bytes = wos[0].numel() * 2 + B * (HEADS * 128 + mla.MODEL_DIM) * 2
+        oproj = {"us": op_ms * 1e3, "bytes_per_launch": op_bytes, "achieved_GBps": op_bytes / (op_ms * 1e-3) / 1e9,
+                 "frac_hbm": op_bytes / (op_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "tflops": 2.0 * B * HEADS * 128 * mla.MODEL_DIM / (op_ms * 1e-3) / 1e12,
+                 "kernel": "mla_output_proj", "weights": "bf16 [7168, 16384], 3 rotated copies"}
+        log(f"output projection: {op_ms * 1e3:.2f} us ({oproj['achieved_GBps']:.0f} GB/s)")
+        del ox, wos, oout
     log(f"{args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us), "
         f"median of 5 trials {sorted(trials)[2] * 1e3:.2f} us, warm (no rotation) {warm_ms * 1e3:.2f} us; "
         f"decode kernel {decode_ms * 1e3:.2f} us, decode + combine {attn_ms * 1e3:.2f} us; "
@@ -340,6 +365,8 @@ def main():
         ridge_spec = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         ridge_meas = pk["mfma_bf16_TFLOPs"] * 1e12 / (pk["row_gather_GBps"] * 1e9)
         attain = dict(pk)
+        if oproj is not None:
+            oproj["frac_vs_stream_read"] = oproj["achieved_GBps"] / pk["stream_read_GBps"]
         attain.update({
             "decode_frac_vs_row_gather": dec_gbs / pk["row_gather_GBps"],
             "decode_mfma_frac_vs_measured": dec_tflops / pk["mfma_bf16_TFLOPs"],
@@ -396,6 +423,7 @@ def main():
         "attention_only": {"value": B / (attn_ms * 1e-3), "unit": "queries/s", "us": attn_ms * 1e3,
                            "kernels": "mla_sparse_decode + mla_combine" if bufs.num_splits > 1
                            else "mla_sparse_decode"},
+        "output_proj": oproj,
         "attainable": attain,
         "parity_sampled_rel_err": parity,
         "cpu_baseline": cpu,
