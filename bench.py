@@ -4,32 +4,34 @@
 
 One step = mla_absorb_q + mla_sparse_decode + (mla_combine + mla_value_up, as
 the single fused mla_combine_value_up launch when the plan splits the keys)
-over a batch of B single-token queries, all inputs resident in HBM.  Input sets are
-rotated (distinct index sets, queries and weight copies; whole caches when they
-are small) so that every cycle moves >= 1 GB and the 256 MB memory-side cache
-cannot serve a repeated step.  Prints ONE JSON line.
+over a batch of B single-token queries, all inputs resident in HBM.  Input
+sets are rotated, each with its own lengths, index sets, queries, weights and
+whole cache, so that every cycle moves >= 1 GB of distinct bytes (printed)
+and the 256 MB memory-side cache cannot serve a repeated step.  Each step's C
+calls are made with arguments marshalled once per input set
+(binding.StepLauncher).  Prints ONE JSON line.
+
+`value` and `ms_per_step` come from the median of five trials of K rotated
+steps, each bracketed by two HIP events with nothing recorded inside; the
+five trials and the host's enqueue time per step in each are listed.
 
 The roofline entry is for the dominant kernel (the sparse decode): its
 algorithmic bytes per launch (selected cache rows at 1152 B + 4 B per index)
 over its mean launch time, from HIP events bracketing K decode launches
 issued back to back on its stream over the same rotating input sets (their
-absorbed queries computed beforehand; the throughput pass has no events
-inside the steps, and an event pair around every launch would add ~3 us).
+absorbed queries computed beforehand).
 The line also carries the per-head-query rate (128 x queries/s), the
 attention-only rate (B over the mean time of decode + the separate split
-combine, K pairs back to back; value-up excluded), the per-step time of five
-trials of the K rotated steps (the value is the first's) and their median, a
-warm figure labelled as such (one input set every step), and the attainable
-peaks measured on the same GPU (sparse_mla_amd/peaks.py: streaming read, the
-decode's row gather on random rows, dense bf16 MFMA) with the decode's
-fraction of them and the side of both ridges its intensity falls on.
+combine, K pairs back to back; value-up excluded), a warm figure labelled as
+such (one input set every step), and the attainable peaks measured on the
+same GPU (sparse_mla_amd/peaks.py: streaming read, the decode's row gather on
+random rows, dense bf16 MFMA) with the decode's fraction of them and the side
+of both ridges its intensity falls on.
 The CPU baseline runs the fp64 oracle (oracle/, test infrastructure) on a
 bounded sample of the same workload.
 
-The default warm-up is long (1000 steps, tens of ms): for the first tens of
-milliseconds of back-to-back steps the GPU runs the step about 10 % slower
-than in steady state (20 warm-up steps: 71 us/step; 1000: 64.5 us/step at
-B=64, k=2048), and a decode loop runs in steady state.
+The default warm-up is long (1000 steps, tens of ms), so that the timed
+steps run in the GPU's steady state.
 """
 from __future__ import annotations
 
@@ -111,19 +113,12 @@ def copy_calibration(torch):
 
 
 def make_sets(name, R, torch, workload):
-    """R input sets of one workload.  Large caches are shared and only the
-    index sets, queries and weights rotate; small caches rotate too."""
-    spec = workload.SPECS[name]
-    cache_bytes = spec.B * spec.L * ROW_BYTES
-    base = workload.make(name, device="cpu", cache_device="cuda")
+    """R independent input sets of one workload: each draws its own lengths,
+    index sets, queries, weights and whole cache (variant seeds), so no two
+    sets share a selected row, a recent-token window or a weight byte."""
     sets = []
     for v in range(R):
-        if v == 0:
-            w = base
-        else:
-            shared = base.cache if cache_bytes > (1 << 28) else None
-            w = workload.make(name, device="cpu", cache_device="cuda", variant=v, lens=base.seq_lens.cpu(),
-                              cache=shared)
+        w = workload.make(name, device="cpu", cache_device="cuda", variant=v)
         dev = {}
         for key in ("q_nope", "q_pe", "wkv_b", "indices", "wkv_b_fp8", "wkv_b_scale", "seq_lens"):
             t = getattr(w, key)
@@ -132,6 +127,19 @@ def make_sets(name, R, torch, workload):
         w.wkv_b_fp8, w.wkv_b_scale, w.seq_lens = dev["wkv_b_fp8"], dev["wkv_b_scale"], dev["seq_lens"]
         sets.append(w)
     return sets
+
+
+def step_bytes_of(w, torch):
+    """Algorithmic HBM bytes of one step over input set w: the selected rows,
+    both weight slices, the queries, the outputs and the index lists."""
+    if w.indices is None:
+        keys = int(w.seq_lens.sum().item())
+        idx_bytes = 0
+    else:
+        keys = int((w.indices >= 0).sum().item())
+        idx_bytes = 4 * keys
+    return keys, keys * ROW_BYTES + idx_bytes, keys * ROW_BYTES + idx_bytes + WEIGHT_BYTES + \
+        w.B * (Q_BYTES_PER_QUERY + O_BYTES_PER_QUERY)
 
 
 def cpu_baseline(w, n_seq, torch, workload):
@@ -206,64 +214,51 @@ def main():
     k_max = w0.k_max
     bufs = mla.DecodeBuffers.allocate(B, k_max, dense, num_splits=args.splits)
     stream = torch.cuda.current_stream()
-
-    def step(w):
-        mla.mla_absorb_q(w.q_nope, w.wkv_b, bufs.q_abs)
-        mla.mla_sparse_decode(bufs.q_abs, w.q_pe, w.kv, w.pe, w.seq_lens, w.max_len, w.indices, w.scale,
-                              bufs.num_splits, bufs.workspace, bufs.o_latent, bufs.lse,
-                              k_max=k_max)
-        if bufs.num_splits > 1:
-            mla.mla_combine_value_up(bufs.workspace, B, bufs.num_splits, w.wkv_b, bufs.out, lse=bufs.lse)
-        else:
-            mla.mla_value_up(bufs.o_latent, w.wkv_b, bufs.out)
+    # One step's three C calls per input set, their arguments marshalled once.
+    launchers = [mla.StepLauncher(bufs, w.q_nope, w.q_pe, w.kv, w.pe, w.wkv_b, w.seq_lens, w.max_len, w.indices,
+                                  w.scale) for w in sets]
+    per_set = [step_bytes_of(w, torch) for w in sets]
+    distinct_bytes = sum(p[2] for p in per_set)
+    log(f"{distinct_bytes / 1e9:.2f} GB of distinct algorithmic bytes per rotation cycle of {R} sets")
 
     for i in range(args.warmup):
-        step(sets[i % R])
+        launchers[i % R]()
     torch.cuda.synchronize()
 
-    # Pass 1 (throughput): K steps bracketed by two events, nothing inside --
-    # an event pair around every decode launch adds ~5 us to each step.
+    # Five trials of K rotated steps, each bracketed by two events with
+    # nothing recorded inside (an event pair around every decode launch adds
+    # ~5 us to each step); `value` is from the median trial.  The host time
+    # to enqueue each trial's K steps is recorded beside it: when it is close
+    # to the GPU time, the host's launch rate sets the pace.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(sets[i % R])
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    # Four more trials of the same K rotated steps (pass 1 is the first); the
-    # line's value stays pass 1's, the median of the five is reported beside it.
-    trials = [ms_step]
-    for _ in range(4):
+    trials, enqueue = [], []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         start.record(stream)
         for i in range(args.steps):
-            step(sets[i % R])
+            launchers[i % R]()
         end.record(stream)
+        enqueue.append((time.perf_counter() - t0) / args.steps)
         torch.cuda.synchronize()
         trials.append(start.elapsed_time(end) / args.steps)
+    ms_step = sorted(trials)[2]
     # A warm figure, labelled as such: the same input set every step, so the
     # 256 MB memory-side cache can serve what the rotation keeps it from.
     start.record(stream)
     for i in range(args.steps):
-        step(sets[0])
+        launchers[0]()
     end.record(stream)
     torch.cuda.synchronize()
     warm_ms = start.elapsed_time(end) / args.steps
     last_set = sets[0]  # bufs.out holds the output of the warm pass's last step
     # Pass 2 (kernel time for the roofline): K decode launches back to back on
-    # the same stream, cycling the input sets (their absorbed queries computed
-    # beforehand), bracketed by two HIP events.  An event pair around every
-    # launch would add ~3 us to each; back to back, the mean includes the
-    # short gap between consecutive launches and nothing else.
-    qabs = [mla.mla_absorb_q(w.q_nope, w.wkv_b) for w in sets]
-
+    # the same stream, cycling the input sets, bracketed by two HIP events.
+    # An event pair around every launch would add ~3 us to each; back to
+    # back, the mean includes the short gap between consecutive launches and
+    # nothing else.
     def decode_only(i):
-        w = sets[i % R]
-        mla.mla_sparse_decode(qabs[i % R], w.q_pe, w.kv, w.pe, w.seq_lens, w.max_len, w.indices, w.scale,
-                              bufs.num_splits, bufs.workspace, bufs.o_latent, bufs.lse, k_max=k_max)
+        launchers[i % R].decode()
 
     for i in range(min(args.warmup, 100)):
         decode_only(i)
@@ -278,9 +273,8 @@ def main():
     # split combine that yields the normalised latent output and its LSE, K
     # pairs back to back; value-up is left out.
     def attention_only(i):
-        decode_only(i)
-        if bufs.num_splits > 1:
-            mla.mla_combine(bufs.workspace, B, bufs.num_splits, bufs.o_latent, lse=bufs.lse)
+        launchers[i % R].decode()
+        launchers[i % R].combine()
 
     for i in range(min(args.warmup, 100)):
         attention_only(i)
@@ -314,21 +308,17 @@ def main():
                  "kernel": "mla_output_proj", "weights": "bf16 [7168, 16384], 3 rotated copies"}
         log(f"output projection: {op_ms * 1e3:.2f} us ({oproj['achieved_GBps']:.0f} GB/s)")
         del ox, wos, oout
-    log(f"{args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e6 / args.steps:.2f} us), "
-        f"median of 5 trials {sorted(trials)[2] * 1e3:.2f} us, warm (no rotation) {warm_ms * 1e3:.2f} us; "
-        f"decode kernel {decode_ms * 1e3:.2f} us, decode + combine {attn_ms * 1e3:.2f} us; "
-        f"plan splits={bufs.num_splits}")
+    log(f"{args.steps} steps x 5 trials: " + ", ".join(f"{t * 1e3:.2f}" for t in trials) +
+        f" us/step (median {ms_step * 1e3:.2f}); host enqueue " + ", ".join(f"{t * 1e6:.1f}" for t in enqueue) +
+        f" us/step; warm (no rotation) {warm_ms * 1e3:.2f} us; decode kernel {decode_ms * 1e3:.2f} us, "
+        f"decode + combine {attn_ms * 1e3:.2f} us; plan splits={bufs.num_splits}")
 
-    # Algorithmic work.
-    if dense:
-        keys = int(w0.seq_lens.sum().item())
-        idx_bytes = 0
-    else:
-        keys = int((w0.indices >= 0).sum().item())
-        idx_bytes = 4 * keys
-    dec_bytes = keys * ROW_BYTES + idx_bytes
+    # Algorithmic work per step: the mean over the K steps of a trial (step i
+    # runs input set i % R; the decode pass cycles the sets the same way).
+    keys = sum(per_set[i % R][0] for i in range(args.steps)) / args.steps
+    dec_bytes = sum(per_set[i % R][1] for i in range(args.steps)) / args.steps
+    step_bytes = sum(per_set[i % R][2] for i in range(args.steps)) / args.steps
     dec_flops = keys * FLOP_PER_KEY
-    step_bytes = dec_bytes + WEIGHT_BYTES + B * (Q_BYTES_PER_QUERY + O_BYTES_PER_QUERY)
     step_flops = dec_flops + B * 2 * (2 * 128 * 128 * 512)
     dec_gbs = dec_bytes / (decode_ms * 1e-3) / 1e9
     dec_tflops = dec_flops / (decode_ms * 1e-3) / 1e12
@@ -403,9 +393,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": name, "B": B, "k_max": k_max, "selected_keys": keys,
-            "cache": f"[{B}, {spec.L}, 576] bf16 packed rows", "rotating_sets": R,
-            "num_splits": bufs.num_splits,
+            "workload": name, "B": B, "k_max": k_max, "selected_keys_mean": keys,
+            "cache": f"[{B}, {spec.L}, 576] bf16 packed rows, one per input set", "rotating_sets": R,
+            "distinct_bytes_per_cycle": distinct_bytes, "num_splits": bufs.num_splits,
         },
         "roofline": {
             "bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -417,7 +407,8 @@ def main():
         "step_roofline_frac": step_roof_s / (ms_step * 1e-3),
         "head_queries_per_s": HEADS * B / (ms_step * 1e-3),
         "trials_us_per_step": [t * 1e3 for t in trials],
-        "median_of_5_us_per_step": sorted(trials)[2] * 1e3,
+        "value_from": "median of the 5 trials",
+        "host_enqueue_us_per_step": [t * 1e6 for t in enqueue],
         "warm_no_rotation": {"value": B / (warm_ms * 1e-3), "unit": "queries/s", "us_per_step": warm_ms * 1e3,
                              "note": "input set 0 every step (cache-warm; not the headline)"},
         "attention_only": {"value": B / (attn_ms * 1e-3), "unit": "queries/s", "us": attn_ms * 1e3,

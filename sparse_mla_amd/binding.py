@@ -306,3 +306,81 @@ def decode_step(bufs: DecodeBuffers, q_nope, q_pe, kv, pe, wkv_b, seq_lens, max_
                     stream=stream)
         mla_value_up(bufs.o_latent, wkv_b, bufs.out, stream=stream)
     return bufs.out
+
+
+class StepLauncher:
+    """One decode step's C calls with their arguments marshalled once.
+
+    Built from the same tensors as ``decode_step`` (their dtypes and shapes
+    checked here, nothing enqueued), it keeps the raw ctypes argument tuples
+    of mla_absorb_q, mla_sparse_decode and mla_combine_value_up (or
+    mla_value_up when the plan has one split), so that each step costs three
+    foreign calls and no Python-side work; the library still checks every
+    argument on each call.  The tensors must stay alive and unchanged while
+    the launcher is used.  Calling it enqueues one step on ``stream`` and
+    raises on a non-zero status."""
+
+    def __init__(self, bufs: DecodeBuffers, q_nope, q_pe, kv, pe, wkv_b, seq_lens, max_len, indices, scale,
+                 stream=None):
+        for t, name, dt in ((q_nope, "q_nope", torch.bfloat16), (q_pe, "q_pe", torch.bfloat16),
+                            (kv, "kv", torch.bfloat16), (pe, "pe", torch.bfloat16), (wkv_b, "wkv_b", torch.bfloat16),
+                            (seq_lens, "seq_lens", torch.int32)):
+            _need(t, name, dt)
+        B = bufs.B
+        if (_bsh(q_nope)[:2] != (B, HEADS) or _bsh(q_pe)[:2] != (B, HEADS) or q_nope.shape[-1] != NOPE
+                or q_pe.shape[-1] != ROPE or kv.dim() != 3 or pe.dim() != 3 or kv.shape[-1] != LATENT
+                or pe.shape[-1] != ROPE or kv.shape[0] < B or pe.shape[0] < B or seq_lens.shape != (B,)
+                or kv.shape[1] < max_len or pe.shape[1] < max_len
+                or tuple(wkv_b.shape) != (HEADS * (NOPE + VALUE), LATENT) or not wkv_b.is_contiguous()):
+            raise ValueError("shape mismatch with the fixed model dimensions or the buffers")
+        if indices is not None:
+            _need(indices, "indices", torch.int32, 2)
+            if not indices.is_contiguous() or indices.shape[0] != B:
+                raise ValueError("indices must be a contiguous int32 [B, k] tensor")
+        st = _stream(stream)
+        B = bufs.B
+        _, _, qn_sb, qn_sh = _bsh(q_nope)
+        _, _, qp_sb, qp_sh = _bsh(q_pe)
+        _, _, o_sb, o_sh = _bsh(bufs.out)
+        ws_bytes = 0 if bufs.workspace is None else bufs.workspace.numel()
+        k_max = bufs.k_max if indices is None else indices.shape[1]
+        self._calls = [
+            (_absorb, "mla_absorb_q", (_ptr(q_nope), qn_sb, qn_sh, _ptr(wkv_b), _ptr(bufs.q_abs), B, st)),
+            (_decode, "mla_sparse_decode", (
+                _ptr(bufs.q_abs), _ptr(q_pe), qp_sb, qp_sh,
+                _ptr(kv), kv.stride(0), kv.stride(1), _ptr(pe), pe.stride(0), pe.stride(1),
+                _ptr(seq_lens), int(max_len), _ptr(indices), int(k_max), float(scale), B,
+                bufs.num_splits, _ptr(bufs.workspace), ws_bytes, _ptr(bufs.o_latent), _ptr(bufs.lse),
+                0, None, 0, None, None, st)),
+        ]
+        if bufs.num_splits > 1:
+            self._calls.append((_combine_value_up, "mla_combine_value_up", (
+                _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits, _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh,
+                _ptr(bufs.lse), None, st)))
+        else:
+            self._calls.append((_value_up, "mla_value_up", (
+                _ptr(bufs.o_latent), _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh, B, st)))
+        # The separate merge of the split partials (for timing the attention
+        # part alone): mla_combine into bufs.o_latent and bufs.lse.
+        self._combine = (_combine, "mla_combine", (_ptr(bufs.workspace), ws_bytes, B, bufs.num_splits,
+                                                   _ptr(bufs.o_latent), _ptr(bufs.lse), None, st))
+
+    @staticmethod
+    def _run(call):
+        fn, name, args = call
+        r = fn(*args)
+        if r:
+            _check(name, r)
+
+    def __call__(self):
+        for call in self._calls:
+            self._run(call)
+
+    def decode(self):
+        """Only the mla_sparse_decode call of the step (reads bufs.q_abs as
+        the last absorb left it)."""
+        self._run(self._calls[1])
+
+    def combine(self):
+        """mla_combine of the split partials (a no-op with one split)."""
+        self._run(self._combine)

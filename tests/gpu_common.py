@@ -9,10 +9,25 @@ from sparse_mla_amd import workload
 
 # Target tolerance: max |O - O_ref| <= 1e-2 * max |O_ref| (the same bar is
 # used for the absorbed query and the latent mix); softmax rows sum to one
-# within 1e-3 (checked on the kernel's own scores and LSE, with the LSE itself
-# held to the oracle's within lse_tol).
+# within 1e-3.  The row sums are checked three ways, each at 1e-3:
+#  - the oracle's exact scores through the kernel's log-sum-exp,
+#    sum_t exp(s_ref,t - LSE_gpu), for every row whose softmax spreads over
+#    at least EXACT_ROWSUM_MIN_NEFF effective keys (n_eff = 1 / sum_t A_t^2
+#    from the oracle's weights; every row of the five workloads does);
+#  - for every row, the oracle's scores recomputed with the absorbed query
+#    rounded to bf16 (the precision the kernels keep it in) through the
+#    kernel's log-sum-exp;
+#  - where the kernel writes its own scores, those through its log-sum-exp.
+# The bf16 rounding of the absorbed query perturbs every score; the row sum
+# against exact scores moves by exp(LSE_ref - LSE_gpu) - 1, which averages
+# out over the keys the softmax spreads over: computed from the oracle
+# alone (its scores with the query rounded), up to 3.4e-4 with 2048 N(0, 1)
+# keys, 1.0e-3 with 64 (about 5 effective keys) and 1.1e-3 with 1000 keys
+# whose weight sits on a few planted spikes; over every row of the parity
+# inputs with at least 64 effective keys, at most 5.5e-4.
 REL_TOL = 1e-2
 ROWSUM_TOL = 1e-3
+EXACT_ROWSUM_MIN_NEFF = 64
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
@@ -48,56 +63,102 @@ def oracle_ref(w: workload.Workload, rows=None, want_weights=False):
                          want_weights=want_weights, want_attended=True, att_len=cache.shape[1])
 
 
-def lse_bound(q_abs_ref, latents, scale: float) -> np.ndarray:
-    """Per-(row, head) bound on |LSE_gpu - LSE_ref|, from oracle quantities only.
-
-    The one rounding ahead of the scores is q~ to bf16 (the absorb output): a
-    round-to-nearest bf16 value errs by at most 2^-9 of its magnitude, so the
-    score of key t errs by at most scale * sum_c 2^-9 |q~_c| |c_t,c| (the
-    rotary half is exact bf16 input).  LSE is a smooth maximum of the scores
-    and moves by at most the largest score error.  The bound doubles that for
-    the kernel's fp32 accumulation and adds 1e-5 for the LSE arithmetic.
-    ``latents[i]`` holds the selected latent rows [n_i, 512] of row i."""
-    qa = np.abs(np.asarray(q_abs_ref, dtype=np.float64))  # [rows, H, 512]
-    tol = np.zeros(qa.shape[:2])
-    for i, c in enumerate(latents):
-        if len(c):
-            tol[i] = scale * 2.0 ** -8 * (qa[i] @ np.abs(np.asarray(c, dtype=np.float64)).T).max(axis=1)
-    return tol + 1e-5
+def rowsum_dev(scores: np.ndarray, lse_gpu: np.ndarray) -> float:
+    """max over (b, h) of |sum_t exp(s[t] - LSE_gpu) - 1| over the index slots
+    (masked slots carry -inf and contribute 0; rows whose LSE is -inf, an
+    empty selection, are skipped).  With the oracle's scores this is the
+    normalisation of the softmax the kernel applied, measured against the
+    exact scores; with the kernel's own scores, its self-consistency."""
+    s = np.asarray(scores, dtype=np.float64)
+    lse = np.asarray(lse_gpu, dtype=np.float64)
+    ok = np.isfinite(lse)
+    if not ok.any():
+        return 0.0
+    tot = np.exp(s - np.where(ok, lse, 0.0)[..., None]).sum(-1)
+    return float(np.max(np.abs(tot[ok] - 1.0)))
 
 
-def selected_latents(w: workload.Workload, rows=None):
-    """The selected in-range latent rows of each sequence of a CPU-side workload."""
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 (ties to even), in fp64."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    return t.to(torch.bfloat16).double().numpy()
+
+
+def bf16_query_scores(ref, q_pe, rows, scale: float) -> np.ndarray:
+    """The oracle's scores with its absorbed query rounded to bf16:
+    scale * (bf16(q~_ref) . c_t + q_pe . k_pe_t) per index slot, -inf where
+    ref["scores"] is -inf.  rows[i] holds the cache rows [k, 576] named by
+    sequence i's index slots (any row where the slot is masked)."""
+    qa = bf16_round(ref["q_abs"])                                   # [n, H, 512]
+    qp = f64(q_pe).reshape(qa.shape[0], qa.shape[1], -1)
+    out = np.empty_like(ref["scores"])
+    for i, r in enumerate(rows):
+        r = f64(r) if isinstance(r, torch.Tensor) else np.asarray(r, dtype=np.float64)
+        out[i] = scale * (qa[i] @ r[:, :qa.shape[2]].T + qp[i] @ r[:, qa.shape[2]:].T)
+    return np.where(np.isneginf(ref["scores"]), -np.inf, out)
+
+
+def check_rowsums(ref, lse_gpu, own_scores=None, q16_scores=None, all_exact=False):
+    """The row-sum checks described at the top of this module; with
+    all_exact every row is held to the exact-score bar (the workloads at
+    full size).  Returns the largest exact-score deviation over all rows."""
+    lse = np.asarray(lse_gpu, dtype=np.float64)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref["lse"])), "empty rows differ"
+    n_eff = 1.0 / np.maximum((np.asarray(ref["weights"]) ** 2).sum(-1), 1e-300)   # [n, H]
+    big = n_eff >= EXACT_ROWSUM_MIN_NEFF
+    if all_exact:
+        big = np.ones_like(big)
+    s = np.asarray(ref["scores"], dtype=np.float64)
+    ok = np.isfinite(lse)
+    with np.errstate(invalid="ignore"):
+        tot = np.exp(s - np.where(ok, lse, 0.0)[..., None]).sum(-1)
+    dev = np.where(ok, np.abs(tot - 1.0), 0.0)
+    if big.any():
+        worst = float(dev[big].max())
+        assert worst <= ROWSUM_TOL, f"oracle-score row sum off by {worst:.2e}"
+    if q16_scores is not None:
+        d16 = rowsum_dev(q16_scores, lse)
+        assert d16 <= ROWSUM_TOL, f"bf16-query oracle-score row sum off by {d16:.2e}"
+    if own_scores is not None:
+        dev_own = rowsum_dev(own_scores, lse)
+        assert dev_own <= ROWSUM_TOL, f"kernel-score row sum off by {dev_own:.2e}"
+    return float(dev.max())
+
+
+def slot_rows(w: workload.Workload, rows=None):
+    """Cache rows [k, 576] named by each index slot of sequences ``rows`` of a
+    CPU-side workload (row 0 where a slot is masked; dense mode: positions
+    0 .. max_len - 1), in the slot order of oracle_ref's scores."""
     rows = list(range(w.B)) if rows is None else list(rows)
-    cache = w.cache.cpu()
+    cache = w.cache.cpu().double().numpy()
     out = []
     for b in rows:
-        L = int(w.seq_lens[b])
         if w.indices is None:
-            pos = np.arange(L)
+            pos = np.arange(w.max_len)
         else:
-            idx = w.indices.cpu()[b].numpy()
-            pos = np.unique(idx[(idx >= 0) & (idx < L)])
-        out.append(cache[b, torch.from_numpy(pos), :workload.DC].double().numpy())
+            pos = w.indices.cpu()[b].numpy().astype(np.int64)
+        pos = np.where((pos >= 0) & (pos < cache.shape[1]), pos, 0)
+        out.append(cache[b, pos])
     return out
 
 
-def lse_tol(w: workload.Workload, ref, rows=None) -> np.ndarray:
-    return lse_bound(ref["q_abs"], selected_latents(w, rows), w.scale)
-
-
-def lse_dev(lse_gpu: np.ndarray, ref) -> np.ndarray:
-    """|LSE_gpu - LSE_ref| with equal infinities counting as zero."""
-    a, r = np.asarray(lse_gpu, dtype=np.float64), np.asarray(ref["lse"], dtype=np.float64)
-    same = (a == r)
-    return np.where(same, 0.0, np.abs(a - r))
-
-
-def rowsum_dev(ref_scores: np.ndarray, lse_gpu: np.ndarray) -> float:
-    """max over (b,h) of |sum_t exp(s_ref[t] - LSE_gpu) - 1| over the selected slots
-    (masked slots carry -inf and contribute 0)."""
-    s = np.exp(ref_scores - lse_gpu[..., None])
-    return float(np.max(np.abs(s.sum(-1) - 1.0)))
+def attended_sets_equal(bitmap: torch.Tensor, w: workload.Workload):
+    """The attended bitmap against every row's set of selected in-range
+    positions (np.unique of its index list; 0 .. L_b - 1 in dense mode)."""
+    bits = bitmap.cpu().numpy().view(np.uint32)
+    lens = w.seq_lens.cpu().numpy()
+    idx = None if w.indices is None else w.indices.cpu().numpy()
+    for b in range(w.B):
+        got = np.unpackbits(bits[b].view(np.uint8), bitorder="little")
+        got_pos = np.nonzero(got)[0]
+        if idx is None:
+            exp_pos = np.arange(int(lens[b]))
+        else:
+            r = idx[b]
+            exp_pos = np.unique(r[(r >= 0) & (r < lens[b])])
+        if not np.array_equal(got_pos, exp_pos):
+            return False
+    return True
 
 
 def gather_rows_for_oracle(w, rows):
