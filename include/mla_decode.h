@@ -32,8 +32,9 @@
  *  - Every entry point returns MLA_OK (0) or a positive mla_status.  Argument
  *    errors are detected on the host before anything is enqueued.  No C++
  *    exception crosses this interface and the library never aborts.
- *  - The library is reentrant; its only global state is a per-device cache of
- *    the compute-unit count.
+ *  - The library is reentrant.  Its only global state is the static scratch
+ *    array of mla_sparse_decode_noalloc (one per GPU, with its address looked
+ *    up once per device).
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -65,7 +66,8 @@ typedef enum {
   MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < mla_workspace_bytes(B, num_splits)   */
   MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths     */
   MLA_ERR_HIP = 6,                 /* a HIP call failed: see mla_last_hip_error()     */
-  MLA_ERR_RANGE = 7                /* one sequence's cache or q_pe span exceeds 2 GiB */
+  MLA_ERR_RANGE = 7,               /* one sequence's cache or q_pe span exceeds 2 GiB */
+  MLA_ERR_SCRATCH_LIMIT = 8        /* partials larger than the static scratch (noalloc) */
 } mla_status;
 
 /* Flags of mla_sparse_decode. */
@@ -161,6 +163,34 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
                       void* o_latent, float* lse,
                       uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
                       float* scores_out, uint32_t* status_dev, void* stream);
+
+/*
+ * Step 2 (and 3) for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same decode as mla_sparse_decode, with the same arguments except that
+ * there is no workspace.  With num_splits > 1 the split partials go to a
+ * static device array inside the library (mla_noalloc_scratch_bytes() bytes
+ * per GPU, held until the process ends) and this call also merges them, as
+ * mla_combine does, into o_latent and lse; with num_splits == 1 it is
+ * mla_sparse_decode.  It calls no allocator.
+ * Errors: those of mla_sparse_decode, and MLA_ERR_SCRATCH_LIMIT when
+ * mla_workspace_bytes(B, num_splits) exceeds the scratch (40 MiB: e.g.
+ * B = 64 with 4 splits needs 33.8 MB).  The first call on a device looks up
+ * the scratch address (MLA_ERR_HIP if that fails).
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised by
+ * the caller.  Nothing in the scratch needs clearing between calls: the
+ * decode overwrites every partial it merges.
+ */
+size_t mla_noalloc_scratch_bytes(void);
+int mla_sparse_decode_noalloc(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                              const void* kv, int64_t kv_sb, int64_t kv_st,
+                              const void* pe, int64_t pe_sb, int64_t pe_st,
+                              const int32_t* seq_lens, int32_t max_len,
+                              const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                              int32_t num_splits, void* o_latent, float* lse,
+                              uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                              float* scores_out, uint32_t* status_dev, void* stream);
 
 /*
  * Step 3: merge the S partials of step 2 ("Softmax" page: the normalisation

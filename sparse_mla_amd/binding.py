@@ -57,6 +57,11 @@ _decode = _sig("mla_sparse_decode", ctypes.c_int, [
     _u32, _p, _i64,                # flags bitmap bitmap_words
     _p, _p, _p,                    # scores status stream
 ])
+_decode_noalloc = _sig("mla_sparse_decode_noalloc", ctypes.c_int, [
+    _p, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32, _f32, _i32,
+    _i32, _p, _p, _u32, _p, _i64, _p, _p, _p,
+])
+_noalloc_scratch_bytes = _sig("mla_noalloc_scratch_bytes", _sz, [])
 _combine = _sig("mla_combine", ctypes.c_int, [_p, _sz, _i32, _i32, _p, _p, _p, _p])
 _value_up = _sig("mla_value_up", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p])
 _combine_value_up = _sig("mla_combine_value_up", ctypes.c_int,
@@ -181,6 +186,52 @@ def mla_sparse_decode(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indices, scal
         _ptr(indices), int(k_max), float(scale), B,
         int(num_splits), _ptr(workspace), ws_bytes,
         _ptr(o_latent), _ptr(lse),
+        int(flags), _ptr(bitmap), words,
+        _ptr(scores), _ptr(status), _stream(stream)))
+
+
+def mla_noalloc_scratch_bytes() -> int:
+    return int(_noalloc_scratch_bytes())
+
+
+def mla_sparse_decode_noalloc(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indices, scale: float,
+                              num_splits: int, o_latent, lse=None, flags: int = 0, bitmap=None, scores=None,
+                              status=None, k_max=None, stream=None):
+    """mla_sparse_decode with the split partials in the library's static
+    scratch and the merge into o_latent / lse done by the same call (no
+    workspace argument, no allocation)."""
+    _need(q_abs, "q_abs", torch.bfloat16, 3)
+    _need(q_pe, "q_pe", torch.bfloat16)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(pe, "pe", torch.bfloat16, 3)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(o_latent, "o_latent", torch.bfloat16, 3)
+    B = q_abs.shape[0]
+    Bq, Hq, qsb, qsh = _bsh(q_pe)
+    if Bq != B or Hq != HEADS or q_pe.shape[-1] != ROPE or kv.shape[-1] != LATENT or pe.shape[-1] != ROPE:
+        raise ValueError("shape mismatch with the fixed model dimensions")
+    if kv.shape[0] < B or pe.shape[0] < B or seq_lens.shape[0] != B or kv.shape[1] < max_len or pe.shape[1] < max_len:
+        raise ValueError("cache or seq_lens too small")
+    if tuple(o_latent.shape) != (B, HEADS, LATENT) or not o_latent.is_contiguous():
+        raise ValueError("o_latent must be a contiguous [B,128,512] tensor")
+    if indices is not None:
+        _need(indices, "indices", torch.int32, 2)
+        if not indices.is_contiguous() or indices.shape[0] != B:
+            raise ValueError("indices must be a contiguous int32 [B, k] tensor")
+        k_max = indices.shape[1]
+    elif k_max is None:
+        k_max = max_len
+    words = 0
+    if bitmap is not None:
+        _need(bitmap, "bitmap", torch.int32, 2)
+        words = bitmap.shape[1]
+    _check("mla_sparse_decode_noalloc", _decode_noalloc(
+        _ptr(q_abs), _ptr(q_pe), qsb, qsh,
+        _ptr(kv), kv.stride(0), kv.stride(1),
+        _ptr(pe), pe.stride(0), pe.stride(1),
+        _ptr(seq_lens), int(max_len),
+        _ptr(indices), int(k_max), float(scale), B,
+        int(num_splits), _ptr(o_latent), _ptr(lse),
         int(flags), _ptr(bitmap), words,
         _ptr(scores), _ptr(status), _stream(stream)))
 

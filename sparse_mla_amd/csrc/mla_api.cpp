@@ -47,6 +47,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "stride smaller than the fixed row width";
     case MLA_ERR_HIP: return "HIP runtime error (see mla_last_hip_error)";
     case MLA_ERR_RANGE: return "a sequence's cache or q_pe span exceeds 2 GiB";
+    case MLA_ERR_SCRATCH_LIMIT: return "the split partials exceed the library's static scratch (mla_noalloc_scratch_bytes)";
     default: return "unknown status";
   }
 }
@@ -110,15 +111,21 @@ int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
   return hip_status(mla::launch_absorb(a, stream));
 }
 
-int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
-                      const void* kv, int64_t kv_sb, int64_t kv_st,
-                      const void* pe, int64_t pe_sb, int64_t pe_st,
-                      const int32_t* seq_lens, int32_t max_len,
-                      const int32_t* indices, int32_t k_max, float scale, int32_t B,
-                      int32_t num_splits, void* workspace, size_t ws_bytes,
-                      void* o_latent, float* lse,
-                      uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
-                      float* scores_out, uint32_t* status_dev, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks and kernel arguments of mla_sparse_decode (shared with the
+// allocation-free variant, which passes its static scratch as the workspace).
+int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                   const void* kv, int64_t kv_sb, int64_t kv_st,
+                   const void* pe, int64_t pe_sb, int64_t pe_st,
+                   const int32_t* seq_lens, int32_t max_len,
+                   const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                   int32_t num_splits, void* workspace, size_t ws_bytes,
+                   void* o_latent, float* lse,
+                   uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                   float* scores_out, uint32_t* status_dev, mla::DecodeArgs* out) {
   if (!q_abs || !q_pe || !kv || !pe || !seq_lens) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536 || k_max < 1 || max_len < 1) return MLA_ERR_BAD_DIM;
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
@@ -149,7 +156,7 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
   }
   if ((flags & MLA_FLAG_WRITE_SCORES) && !scores_out) return MLA_ERR_NULL_POINTER;
 
-  mla::DecodeArgs a;
+  mla::DecodeArgs& a = *out;
   a.q_abs = static_cast<const uint16_t*>(q_abs);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.q_pe_sb = q_pe_sb;
@@ -181,7 +188,73 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
   a.bitmap_words = bitmap_words;
   a.scores = scores_out;
   a.status = status_dev;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                      const void* kv, int64_t kv_sb, int64_t kv_st,
+                      const void* pe, int64_t pe_sb, int64_t pe_st,
+                      const int32_t* seq_lens, int32_t max_len,
+                      const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                      int32_t num_splits, void* workspace, size_t ws_bytes,
+                      void* o_latent, float* lse,
+                      uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                      float* scores_out, uint32_t* status_dev, void* stream) {
+  mla::DecodeArgs a;
+  const int st = prepare_decode(q_abs, q_pe, q_pe_sb, q_pe_sh, kv, kv_sb, kv_st, pe, pe_sb, pe_st, seq_lens,
+                                max_len, indices, k_max, scale, B, num_splits, workspace, ws_bytes, o_latent, lse,
+                                flags, attended_bitmap, bitmap_words, scores_out, status_dev, &a);
+  if (st != MLA_OK) return st;
   return hip_status(mla::launch_decode(a, stream));
+}
+
+size_t mla_noalloc_scratch_bytes(void) { return mla::kScratchBytes; }
+
+int mla_sparse_decode_noalloc(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                              const void* kv, int64_t kv_sb, int64_t kv_st,
+                              const void* pe, int64_t pe_sb, int64_t pe_st,
+                              const int32_t* seq_lens, int32_t max_len,
+                              const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                              int32_t num_splits, void* o_latent, float* lse,
+                              uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                              float* scores_out, uint32_t* status_dev, void* stream) {
+  if (B >= 1 && num_splits > 1 && num_splits <= MLA_MAX_SPLITS &&
+      mla_workspace_bytes(B, num_splits) > mla::kScratchBytes)
+    return MLA_ERR_SCRATCH_LIMIT;
+  // Every argument is checked before the scratch address is looked up (the
+  // placeholder stands for the scratch, which is aligned and large enough);
+  // the partials' pointers are set from the real address after.
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t{256});
+  mla::DecodeArgs a;
+  const int st = prepare_decode(q_abs, q_pe, q_pe_sb, q_pe_sh, kv, kv_sb, kv_st, pe, pe_sb, pe_st, seq_lens,
+                                max_len, indices, k_max, scale, B, num_splits, placeholder, mla::kScratchBytes,
+                                o_latent, lse, flags, attended_bitmap, bitmap_words, scores_out, status_dev, &a);
+  if (st != MLA_OK) return st;
+  if (num_splits > 1 && !o_latent) return MLA_ERR_NULL_POINTER;
+  if (num_splits > 1 && !aligned16(o_latent)) return MLA_ERR_ALIGNMENT;
+  if (num_splits > 1) {
+    void* ws = nullptr;
+    const int e = mla::scratch_buffer(&ws);
+    if (e != 0) return hip_status(e);
+    const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+    a.part_o = static_cast<uint16_t*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<uint16_t*>(ws) + units * MLA_LATENT_DIM);
+  }
+  int r = hip_status(mla::launch_decode(a, stream));
+  if (r != MLA_OK || num_splits == 1) return r;
+  mla::CombineArgs c;
+  c.part_o = a.part_o;
+  c.part_ml = a.part_ml;
+  c.B = B;
+  c.S = num_splits;
+  c.o_latent = static_cast<uint16_t*>(o_latent);
+  c.lse = lse;
+  c.status = (flags & MLA_FLAG_VALIDATE) ? status_dev : nullptr;
+  return hip_status(mla::launch_combine(c, stream));
 }
 
 int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,

@@ -100,4 +100,10 @@ int launch_dequant(const DequantArgs& a, void* stream);
 int launch_output_proj(const OutProjArgs& a, void* stream);
 int device_cu_count(int* cus);
 
+// Static device scratch of mla_sparse_decode_noalloc: kScratchBytes per GPU.
+constexpr size_t kScratchBytes = (size_t)40 << 20;
+// The current device's scratch address (looked up once per device).
+// Returns a hipError_t value (0 on success).
+int scratch_buffer(void** ptr);
+
 }  // namespace mla

@@ -25,6 +25,7 @@
 // K-strided operand fragment.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 #include <math.h>
 #include <stdint.h>
@@ -1354,6 +1355,39 @@ int device_cu_count(int* cus) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return (int)e;
   return (int)hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (mla_sparse_decode_noalloc):
+// the split partials live in this file-scope device array, one copy per GPU,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in symbol): the device address is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept here.
+// ---------------------------------------------------------------------------
+namespace {
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_err[kMaxDevices];
+}  // namespace
+
+int scratch_buffer(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = (int)r;
+    g_scratch_ptr[dev] = r == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != 0) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return 0;
 }
 
 }  // namespace mla

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 LIB = os.path.join(ROOT, "sparse_mla_amd", "libmla_decode.so")
 
-OK, NULLP, BADDIM, ALIGN, WS, UNSUP, HIP, RANGE = range(8)
+OK, NULLP, BADDIM, ALIGN, WS, UNSUP, HIP, RANGE, SCRATCH = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -24,6 +24,9 @@ def lib():
                                  ctypes.c_float, ctypes.c_size_t)
     L.mla_sparse_decode.argtypes = [p, p, i64, i64, p, i64, i64, p, i64, i64, p, i32, p, i32, f32, i32,
                                     i32, p, sz, p, p, u32, p, i64, p, p, p]
+    L.mla_sparse_decode_noalloc.argtypes = [p, p, i64, i64, p, i64, i64, p, i64, i64, p, i32, p, i32, f32, i32,
+                                            i32, p, p, u32, p, i64, p, p, p]
+    L.mla_noalloc_scratch_bytes.restype = sz
     L.mla_absorb_q.argtypes = [p, i64, i64, p, p, i32, p]
     L.mla_value_up.argtypes = [p, p, p, i64, i64, i32, p]
     L.mla_combine.argtypes = [p, sz, i32, i32, p, p, p, p]
@@ -52,8 +55,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.mla_abi_version() == 2
-    for code in range(8):
-        assert lib.mla_status_string(code)
+    for code in range(9):
+        assert lib.mla_status_string(code) != b"unknown status"
     assert lib.mla_last_hip_error() == 0
 
 
@@ -195,3 +198,23 @@ def test_output_proj_host_checks(lib):
     assert lib.mla_output_proj(a, 16388, a, a, 7168, 4, None) == ALIGN     # stride not a multiple of 8
     assert lib.mla_output_proj(a, 16384, a + 8, a, 7168, 4, None) == ALIGN
     assert lib.mla_output_proj(a, 16384, a, a + 1, 7168, 4, None) == ALIGN
+
+
+def test_noalloc_host_checks(lib):
+    """mla_sparse_decode_noalloc rejects plans whose partials exceed its
+    static scratch, and bad arguments, on the host before it looks up the
+    scratch or enqueues anything."""
+    a = FAKE
+    assert lib.mla_noalloc_scratch_bytes() == 40 << 20
+    args = [a, a, 128 * 64, 64, a, 576 * 2048, 576, a + 1024, 576 * 2048, 576, a, 2048, a, 2048, 0.07, 128,
+            64, a, None, 0, None, 0, None, None, None]
+    assert lib.mla_workspace_bytes(128, 64) > lib.mla_noalloc_scratch_bytes()
+    assert lib.mla_sparse_decode_noalloc(*args) == SCRATCH
+    args[15], args[16] = 2, 2          # B = 2, two splits: fits the scratch
+    args[0] = None
+    assert lib.mla_sparse_decode_noalloc(*args) == NULLP
+    args[0] = a
+    args[17] = None                    # o_latent
+    assert lib.mla_sparse_decode_noalloc(*args) == NULLP
+    args[17] = a + 8
+    assert lib.mla_sparse_decode_noalloc(*args) == ALIGN
