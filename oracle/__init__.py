@@ -23,6 +23,7 @@ from .core import (  # noqa: F401
     absorb,
     value_up,
     output_proj,
+    prefill,
     dequant_fp8,
     e4m3_to_double,
     bf16_bits_to_double,

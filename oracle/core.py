@@ -66,6 +66,15 @@ def load(path: str | None = None):
         lib.oracle_absorb.argtypes = [i64, i64, i64, i64, i64, p, p, p]
         lib.oracle_value_up.restype = ctypes.c_int
         lib.oracle_value_up.argtypes = [i64, i64, i64, i64, i64, p, p, p]
+        lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_prefill.argtypes = [
+            i64, i64, i64, i64, i64, i64, i64,   # B T H Dn Dc Dr Dv
+            p, p,                                # q_nope q_pe
+            p, i64, i64,                         # kv kv_sb kv_st
+            p, i64, i64,                         # pe pe_sb pe_st
+            p, p, i64, d,                        # wkv_b indices k_max scale
+            p, p, p,                             # out lse attended
+        ]
         lib.oracle_output_proj.restype = ctypes.c_int
         lib.oracle_output_proj.argtypes = [i64, i64, i64, p, p, p]
         if path is not None:
@@ -162,6 +171,48 @@ def decode(q_nope, q_pe, kv, pe, wkv_b, seq_lens, indices, scale,
     if weights is not None:
         res["weights"] = weights
         res["scores"] = scores
+    if att is not None:
+        res["attended"] = att
+    return res
+
+
+def prefill(q_nope, q_pe, kv, pe, wkv_b, indices, scale, want_attended=False, lib=None):
+    """Sparse prefill in the full-sequence (MHA) form, fp64.
+
+    q_nope [B, T, H, Dn], q_pe [B, T, H, Dr] (queries of the prompt's T
+    positions), kv [B, >=T, Dc], pe [B, >=T, Dr] (latent and rotary key of
+    each prompt position; only the first T are keys), wkv_b [H*(Dn+Dv), Dc],
+    indices [B, T, k] int (the indexer's selection of each query; -1 is
+    padding) or None (every causal key).  Returns a dict with out
+    [B, T, H, Dv], lse [B, T, H], status and, on request, attended
+    [B, T, T] (uint8)."""
+    lib = lib or load()
+    qn = _f64(q_nope)
+    qr = _f64(q_pe)
+    B, T, H, Dn = qn.shape
+    Dr = qr.shape[3]
+    kvd = _f64(kv)
+    ped = _f64(pe)
+    Dc = kvd.shape[2]
+    assert kvd.shape[1] >= T and ped.shape[1] >= T
+    w = _f64(wkv_b)
+    Dv = w.shape[0] // H - Dn
+    assert w.shape == (H * (Dn + Dv), Dc)
+    idx = None if indices is None else _np(indices, np.int64)
+    k_max = 0 if idx is None else idx.shape[2]
+    if idx is not None:
+        assert idx.shape[:2] == (B, T)
+    out = np.empty((B, T, H, Dv))
+    lse = np.empty((B, T, H))
+    att = np.zeros((B, T, T), dtype=np.uint8) if want_attended else None
+    st = lib.oracle_prefill(B, T, H, Dn, Dc, Dr, Dv, _ptr(qn), _ptr(qr),
+                            _ptr(kvd), kvd.shape[1] * Dc, Dc, _ptr(ped), ped.shape[1] * Dr, Dr,
+                            _ptr(w), _ptr(idx), k_max, float(scale), _ptr(out), _ptr(lse), _ptr(att))
+    if st & ORACLE_ERR_ARG:
+        raise ValueError("oracle_prefill: bad arguments")
+    if st & ORACLE_ERR_INDEX_RANGE:
+        raise IndexError("oracle_prefill: an index is outside the prompt")
+    res = dict(out=out, lse=lse, status=st)
     if att is not None:
         res["attended"] = att
     return res

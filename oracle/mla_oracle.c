@@ -320,3 +320,114 @@ int oracle_output_proj(int64_t B, int64_t Din, int64_t Dout, const double* x, co
     }
     return ORACLE_OK;
 }
+
+/*
+ * Sparse prefill, the full-sequence (MHA) path ("Queries" page, prefill
+ * mode, mla-prefill excerpt): the latent of every prompt position is
+ * up-projected into per-head keys and values, each head's key joins its
+ * non-rotary part with the shared rotary key, and the scores are scaled,
+ * masked by the indexer's selection and the causal mask, normalised over the
+ * keys and used to mix the values.  Keys are the prompt's own positions
+ * 0 .. T-1 (the excerpt's start_pos = 0); query s may attend key t only if
+ * t <= s (causal mask) and t is named in indices[b][s] (index mask, a
+ * scatter of a constant: a set).  NULL indices select every causal key.
+ *
+ *   q_nope [B][T][H][Dn], q_pe [B][T][H][Dr]          (contiguous)
+ *   kv: latent of (b, t) at kv + b*kv_sb + t*kv_st, Dc values
+ *   pe: rotary key of (b, t) at pe + b*pe_sb + t*pe_st, Dr values
+ *   wkv_b [H*(Dn+Dv)][Dc] as in oracle_decode
+ *   indices [B][T][k_max] or NULL; -1 is padding; an index >= T or < -1 is
+ *       an error; an index t > s is masked by causality.
+ *   out [B][T][H][Dv], lse [B][T][H] (may be NULL),
+ *   attended [B][T][T] (may be NULL): 1 where key t is attended by query s.
+ */
+int oracle_prefill(int64_t B, int64_t T, int64_t H, int64_t Dn, int64_t Dc, int64_t Dr,
+                   int64_t Dv, const double* q_nope, const double* q_pe,
+                   const double* kv, int64_t kv_sb, int64_t kv_st,
+                   const double* pe, int64_t pe_sb, int64_t pe_st,
+                   const double* wkv_b, const int64_t* indices, int64_t k_max,
+                   double scale, double* out, double* lse, unsigned char* attended) {
+    if (B <= 0 || T <= 0 || H <= 0 || Dn <= 0 || Dc <= 0 || Dr < 0 || Dv <= 0 ||
+        !q_nope || !kv || !wkv_b || !out || (Dr > 0 && (!q_pe || !pe)))
+        return ORACLE_ERR_ARG;
+    if (indices && k_max <= 0) return ORACLE_ERR_ARG;
+    if (indices)
+        for (int64_t i = 0; i < B * T * k_max; ++i)
+            if (indices[i] < -1 || indices[i] >= T) return ORACLE_ERR_INDEX_RANGE;
+    int status = ORACLE_OK;
+    for (int64_t b = 0; b < B; ++b) {
+        /* The up-projection of every prompt position: k_nope[t][h][d] and
+         * v[t][h][d] from the latent c_t (the excerpt's wkv_b(kv)). */
+        double* knope = (double*)malloc(sizeof(double) * (size_t)(T * H * Dn));
+        double* v = (double*)malloc(sizeof(double) * (size_t)(T * H * Dv));
+        #pragma omp parallel for schedule(static)
+        for (int64_t th = 0; th < T * H; ++th) {
+            const int64_t t = th / H, h = th % H;
+            const double* c = kv + b * kv_sb + t * kv_st;
+            const double* w_uk = wkv_b + (h * (Dn + Dv)) * Dc;
+            const double* w_uv = wkv_b + (h * (Dn + Dv) + Dn) * Dc;
+            for (int64_t d = 0; d < Dn; ++d) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < Dc; ++j) acc += w_uk[d * Dc + j] * c[j];
+                knope[th * Dn + d] = acc;
+            }
+            for (int64_t d = 0; d < Dv; ++d) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < Dc; ++j) acc += w_uv[d * Dc + j] * c[j];
+                v[th * Dv + d] = acc;
+            }
+        }
+        #pragma omp parallel for schedule(dynamic, 1) reduction(|:status)
+        for (int64_t s = 0; s < T; ++s) {
+            /* The attended keys of query s: selected and not in the future. */
+            unsigned char* mark = (unsigned char*)calloc((size_t)T, 1);
+            if (indices) {
+                const int64_t* row = indices + (b * T + s) * k_max;
+                for (int64_t j = 0; j < k_max; ++j)
+                    if (row[j] >= 0 && row[j] <= s) mark[row[j]] = 1;
+            } else {
+                for (int64_t t = 0; t <= s; ++t) mark[t] = (unsigned char)1;
+            }
+            int64_t n = 0;
+            for (int64_t t = 0; t < T; ++t) n += mark[t];
+            if (n == 0) status |= ORACLE_ERR_EMPTY;
+            if (attended) memcpy(attended + (b * T + s) * T, mark, (size_t)T);
+            double* sc = (double*)malloc(sizeof(double) * (size_t)T);
+            for (int64_t h = 0; h < H; ++h) {
+                const double* qn = q_nope + ((b * T + s) * H + h) * Dn;
+                const double* qr = Dr > 0 ? q_pe + ((b * T + s) * H + h) * Dr : NULL;
+                /* scores over the keys [k_nope | k_pe] of this head, scaled */
+                double m = -INFINITY;
+                for (int64_t t = 0; t < T; ++t) {
+                    if (!mark[t]) { sc[t] = -INFINITY; continue; }
+                    const double* kn = knope + (t * H + h) * Dn;
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < Dn; ++d) acc += qn[d] * kn[d];
+                    if (Dr > 0) {
+                        const double* kr = pe + b * pe_sb + t * pe_st;
+                        for (int64_t r = 0; r < Dr; ++r) acc += qr[r] * kr[r];
+                    }
+                    sc[t] = acc * scale;
+                    if (sc[t] > m) m = sc[t];
+                }
+                double denom = 0.0;
+                for (int64_t t = 0; t < T; ++t) if (mark[t]) denom += exp(sc[t] - m);
+                if (lse) lse[(b * T + s) * H + h] = n > 0 ? log(denom) + m : -INFINITY;
+                double* o = out + ((b * T + s) * H + h) * Dv;
+                for (int64_t d = 0; d < Dv; ++d) o[d] = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    if (!mark[t]) continue;
+                    const double a = exp(sc[t] - m) / denom;
+                    const double* vv = v + (t * H + h) * Dv;
+                    for (int64_t d = 0; d < Dv; ++d) o[d] += a * vv[d];
+                }
+                if (n == 0) for (int64_t d = 0; d < Dv; ++d) o[d] = NAN;
+            }
+            free(sc);
+            free(mark);
+        }
+        free(knope);
+        free(v);
+    }
+    return status;
+}

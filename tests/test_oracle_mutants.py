@@ -73,3 +73,33 @@ def test_output_proj_mutant_fails_the_pin(tmp_path, name, monkeypatch):
     monkeypatch.setattr(oracle, "output_proj", lambda x, wo: real(x, wo, lib=lib))
     with pytest.raises(AssertionError):
         tp.test_output_proj_brute_force()
+
+
+PREFILL_MUTANTS = {
+    "prefill_causal_excludes_diagonal": ("if (row[j] >= 0 && row[j] <= s) mark[row[j]] = 1;",
+                                         "if (row[j] >= 0 && row[j] < s) mark[row[j]] = 1;"),
+    "prefill_rotary_of_query_position": ("const double* kr = pe + b * pe_sb + t * pe_st;",
+                                         "const double* kr = pe + b * pe_sb + s * pe_st;"),
+    "prefill_values_from_w_uk": ("acc += w_uv[d * Dc + j] * c[j];", "acc += w_uk[d * Dc + j] * c[j];"),
+    "prefill_drop_scale": ("sc[t] = acc * scale;", "sc[t] = acc;"),
+    "prefill_transpose_w_uk": ("acc += w_uk[d * Dc + j] * c[j];", "acc += w_uk[j * Dn + d] * c[j];"),
+    "prefill_no_causal_mask": ("for (int64_t t = 0; t <= s; ++t) mark[t] = (unsigned char)1;",
+                               "for (int64_t t = 0; t < T; ++t) mark[t] = (unsigned char)1;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_prefill_mutant_fails_a_pin(tmp_path, name):
+    from tests import pins_prefill
+    lib = _build_mutant(tmp_path, name, *PREFILL_MUTANTS[name])
+
+    def pre(**kw):
+        return oracle.prefill(**kw, lib=lib)
+
+    failed = []
+    for pin in pins_prefill.PREFILL_PINS:
+        try:
+            pin(pre)
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every prefill pin"

@@ -172,3 +172,12 @@ def test_output_proj_selection_at_the_real_shape():
     wo[torch.arange(7168), perm] = 1
     got = oracle.output_proj(x, wo)
     assert np.array_equal(got, x.reshape(2, -1).double().numpy()[:, perm.numpy()])
+
+
+# Prefill oracle (full-sequence MHA form), pinned by tests/pins_prefill.py.
+from tests import pins_prefill  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", pins_prefill.PREFILL_PINS, ids=lambda p: p.__name__)
+def test_prefill_pin(pin):
+    pin(oracle.prefill)
