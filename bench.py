@@ -92,6 +92,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak microbenchmarks")
     ap.add_argument("--no-output-proj", action="store_true", help="skip timing the output projection")
+    ap.add_argument("--no-prefill", action="store_true", help="skip timing the sparse prefill")
     ap.add_argument("--cpu-sample", type=int, default=None, help="sequences in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
@@ -140,6 +141,51 @@ def step_bytes_of(w, torch):
         idx_bytes = 4 * keys
     return keys, keys * ROW_BYTES + idx_bytes, keys * ROW_BYTES + idx_bytes + WEIGHT_BYTES + \
         w.B * (Q_BYTES_PER_QUERY + O_BYTES_PER_QUERY)
+
+
+def prefill_pass(args, mla, workload, torch, stream):
+    """The sparse prefill (mla_sparse_prefill) of one 4096-token prompt, each
+    token selecting 2048 positions, timed on its own (not part of `value`):
+    K launches back to back between two events.  One prompt's cache (4.7 MB)
+    and the weights stay in the GPU's caches across launches: the prefill is
+    bound by the matrix cores, not HBM, so no rotation is needed.  FLOPs are
+    those the absorbed form executes (278 528 per attended key, plus absorb and
+    value-up per token); the full-sequence MHA form of the pages would need
+    81 920 per attended key plus the up-projection of every position."""
+    cfg = workload.PREFILL_HEADLINE
+    B, T, k = cfg["B"], cfg["T"], cfg["k"]
+    p = workload.make_prefill(B, T, k, device="cpu", cache_device="cuda")
+    q_nope, q_pe, wkv_b, idx = (p.q_nope.to("cuda"), p.q_pe.to("cuda"), p.wkv_b.to("cuda"), p.indices.to("cuda"))
+    S = mla.mla_plan(B * T, k, False)
+    ws = torch.empty(mla.mla_prefill_workspace_bytes(B, T, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, T, HEADS, 128), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        mla.mla_sparse_prefill(q_nope, q_pe, p.kv, p.pe, wkv_b, idx, p.scale, num_splits=S, workspace=ws, out=out)
+
+    for _ in range(3):
+        run()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(3, min(args.steps, 20))
+    d0.record(stream)
+    for _ in range(n):
+        run()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    ms = d0.elapsed_time(d1) / n
+    r = p.indices.long()
+    s_pos = torch.arange(T)[None, :, None]
+    keys = int(((r >= 0) & (r <= s_pos)).sum().item())
+    tok_flops = 2 * (2 * 128 * 128 * 512)
+    flops = keys * FLOP_PER_KEY + B * T * tok_flops
+    mha_flops = keys * 2 * 128 * (192 + 128) + B * T * tok_flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"prefill B={B} T={T} k={k}: {ms * 1e3:.1f} us ({B * T / (ms * 1e-3):.0f} tokens/s, {tflops:.0f} TFLOP/s)")
+    return {"workload": f"prefill_b{B}_t{T}_k{k}", "us": ms * 1e3, "tokens_per_s": B * T / (ms * 1e-3),
+            "attended_keys": keys, "num_splits": S, "launches_timed": n,
+            "bound": "mfma", "tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+            "flops_per_launch": flops, "flops_mha_form": mha_flops,
+            "kernels": "mla_sparse_prefill (absorb + causal sparse attention + merge/value-up)"}
 
 
 def cpu_baseline(w, n_seq, torch, workload):
@@ -308,6 +354,9 @@ def main():
                  "kernel": "mla_output_proj", "weights": "bf16 [7168, 16384], 3 rotated copies"}
         log(f"output projection: {op_ms * 1e3:.2f} us ({oproj['achieved_GBps']:.0f} GB/s)")
         del ox, wos, oout
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_pass(args, mla, workload, torch, stream)
     log(f"{args.steps} steps x 5 trials: " + ", ".join(f"{t * 1e3:.2f}" for t in trials) +
         f" us/step (median {ms_step * 1e3:.2f}); host enqueue " + ", ".join(f"{t * 1e6:.1f}" for t in enqueue) +
         f" us/step; warm (no rotation) {warm_ms * 1e3:.2f} us; decode kernel {decode_ms * 1e3:.2f} us, "
@@ -415,6 +464,7 @@ def main():
                            "kernels": "mla_sparse_decode + mla_combine" if bufs.num_splits > 1
                            else "mla_sparse_decode"},
         "output_proj": oproj,
+        "prefill": prefill,
         "attainable": attain,
         "parity_sampled_rel_err": parity,
         "cpu_baseline": cpu,

@@ -227,6 +227,50 @@ int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int3
                          uint32_t* status_dev, void* stream);
 
 /*
+ * Sparse prefill ("Queries" page, prefill mode, mla-prefill excerpt): for
+ * every query token s of a prompt of T tokens, attention over the prompt's
+ * own positions t <= s (the causal mask) that the indexer selected for that
+ * token (the index mask), per head, with keys [W_UK,h c_t | k_pe_t] and
+ * values W_UV,h c_t:
+ *   O[b,s,h,:] = sum_t softmax_t(scale * (q_nope[b,s,h] . W_UK,h c_t +
+ *                                q_pe[b,s,h] . k_pe_t)) W_UV,h c_t.
+ * Computed in the absorbed form, which equals it exactly in real arithmetic
+ * (the "Apply value weights" page, Explanation): mla_absorb_q over the B*T
+ * query rows, the sparse attention of mla_sparse_decode with row r = token
+ * r % T of prompt r / T attending the prompt's latent rows up to its own
+ * position, then the merge and value-up -- three launches on `stream`.
+ *   q_nope  bf16, element (r, h, d) at q_nope[r*q_nope_st + h*q_nope_sh + d]
+ *           for the query rows r = b*T + s ([B,T,128,128] contiguous has
+ *           st = 16384, sh = 128); q_pe likewise with 64 values.
+ *   kv, pe  latent and rotary key of position t of prompt b at
+ *           kv + b*kv_sb + t*kv_st and pe + b*pe_sb + t*pe_st (t < T).
+ *   wkv_b   bf16 [32768][512] as in mla_absorb_q.
+ *   indices int32 [B*T][k_max]: the selection of each query token, any
+ *           order, -1 padding; entries t with s < t < T are removed by the
+ *           causal mask; NULL selects every causal key (then k_max >= T).
+ *   num_splits  key splits per query row (mla_plan(B*T, k_max, ...)).
+ *   workspace   >= mla_prefill_workspace_bytes(B, T, num_splits) bytes.
+ *   out     bf16, element (r, h, d) at out[r*out_st + h*out_sh + d].
+ *   lse     fp32 [B*T][128] (natural log), may be NULL.
+ *   flags   MLA_FLAG_VALIDATE only (attended_bitmap [B*T][bitmap_words],
+ *           bitmap_words >= ceil(T / 32), zeroed by the caller; status_dev:
+ *           an index >= T or below -1 sets MLA_DEV_INDEX_OUT_OF_RANGE);
+ *           MLA_FLAG_WRITE_SCORES returns MLA_ERR_BAD_DIM.
+ * Requires 1 <= B*T <= 65536 and the alignment and span rules of
+ * mla_absorb_q and mla_sparse_decode.
+ */
+size_t mla_prefill_workspace_bytes(int32_t B, int32_t T, int32_t num_splits);
+int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
+                       const void* q_pe, int64_t q_pe_st, int64_t q_pe_sh,
+                       const void* kv, int64_t kv_sb, int64_t kv_st,
+                       const void* pe, int64_t pe_sb, int64_t pe_st,
+                       const void* wkv_b, const int32_t* indices, int32_t k_max, float scale,
+                       int32_t B, int32_t T, int32_t num_splits, void* workspace, size_t ws_bytes,
+                       void* out, int64_t out_st, int64_t out_sh, float* lse,
+                       uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                       uint32_t* status_dev, void* stream);
+
+/*
  * One-time set-up ("Query-key similarity" page, code excerpt: a quantised
  * wkv_b is dequantised once and the dense copy reused):
  *   w_bf16[i][j] = bf16(e4m3(w_fp8[i][j]) * scales[i/128][j/128]), rounded to

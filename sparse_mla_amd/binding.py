@@ -62,6 +62,15 @@ _decode_noalloc = _sig("mla_sparse_decode_noalloc", ctypes.c_int, [
     _i32, _p, _p, _u32, _p, _i64, _p, _p, _p,
 ])
 _noalloc_scratch_bytes = _sig("mla_noalloc_scratch_bytes", _sz, [])
+_prefill_ws = _sig("mla_prefill_workspace_bytes", _sz, [_i32, _i32, _i32])
+_prefill = _sig("mla_sparse_prefill", ctypes.c_int, [
+    _p, _i64, _i64, _p, _i64, _i64,  # q_nope st sh, q_pe st sh
+    _p, _i64, _i64, _p, _i64, _i64,  # kv sb st, pe sb st
+    _p, _p, _i32, _f32,              # wkv_b indices k_max scale
+    _i32, _i32, _i32, _p, _sz,       # B T num_splits workspace ws_bytes
+    _p, _i64, _i64, _p,              # out st sh lse
+    _u32, _p, _i64, _p, _p,          # flags bitmap words status stream
+])
 _combine = _sig("mla_combine", ctypes.c_int, [_p, _sz, _i32, _i32, _p, _p, _p, _p])
 _value_up = _sig("mla_value_up", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p])
 _combine_value_up = _sig("mla_combine_value_up", ctypes.c_int,
@@ -234,6 +243,67 @@ def mla_sparse_decode_noalloc(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indic
         int(num_splits), _ptr(o_latent), _ptr(lse),
         int(flags), _ptr(bitmap), words,
         _ptr(scores), _ptr(status), _stream(stream)))
+
+
+def mla_prefill_workspace_bytes(B: int, T: int, num_splits: int) -> int:
+    return int(_prefill_ws(B, T, num_splits))
+
+
+def _rows_of(t: torch.Tensor, name: str, B: int, T: int, D: int):
+    """(row stride, head stride) of a [B, T, 128, D] tensor whose B*T query
+    rows are evenly spaced (row r = b*T + s at r * row stride)."""
+    if t.dim() != 4 or tuple(t.shape) != (B, T, HEADS, D) or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be [B, T, 128, {D}] with unit inner stride")
+    if B > 1 and t.stride(0) != T * t.stride(1):
+        raise ValueError(f"{name}: the B*T query rows must be evenly spaced")
+    return t.stride(1), t.stride(2)
+
+
+def mla_sparse_prefill(q_nope, q_pe, kv, pe, wkv_b, indices, scale: float, num_splits=None, workspace=None,
+                       out=None, lse=None, flags: int = 0, bitmap=None, status=None, stream=None):
+    """Sparse prefill of B prompts of T tokens: q_nope [B,T,128,128], q_pe
+    [B,T,128,64], kv [B,>=T,512] and pe [B,>=T,64] views of the prompts'
+    latent and rotary keys, indices int32 [B,T,k] (or None: every causal
+    key).  Returns out bf16 [B,T,128,128]."""
+    _need(q_nope, "q_nope", torch.bfloat16)
+    _need(q_pe, "q_pe", torch.bfloat16)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(pe, "pe", torch.bfloat16, 3)
+    _need(wkv_b, "wkv_b", torch.bfloat16, 2)
+    B, T = q_nope.shape[0], q_nope.shape[1]
+    qn_st, qn_sh = _rows_of(q_nope, "q_nope", B, T, NOPE)
+    qp_st, qp_sh = _rows_of(q_pe, "q_pe", B, T, ROPE)
+    if kv.shape[0] < B or pe.shape[0] < B or kv.shape[1] < T or pe.shape[1] < T or kv.shape[2] != LATENT \
+            or pe.shape[2] != ROPE:
+        raise ValueError("kv / pe must cover the B prompts' T positions")
+    if tuple(wkv_b.shape) != (HEADS * (NOPE + VALUE), LATENT) or not wkv_b.is_contiguous():
+        raise ValueError("wkv_b must be a contiguous [32768, 512] tensor")
+    if indices is not None:
+        _need(indices, "indices", torch.int32, 3)
+        if not indices.is_contiguous() or tuple(indices.shape[:2]) != (B, T):
+            raise ValueError("indices must be a contiguous int32 [B, T, k] tensor")
+        k_max = indices.shape[2]
+    else:
+        k_max = T
+    if num_splits is None:
+        num_splits = mla_plan(B * T, k_max, indices is None)
+    ws_need = mla_prefill_workspace_bytes(B, T, num_splits)
+    if workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q_nope.device)
+    if out is None:
+        out = torch.empty((B, T, HEADS, VALUE), dtype=torch.bfloat16, device=q_nope.device)
+    o_st, o_sh = _rows_of(out, "out", B, T, VALUE)
+    words = 0
+    if bitmap is not None:
+        _need(bitmap, "bitmap", torch.int32, 2)
+        words = bitmap.shape[1]
+    _check("mla_sparse_prefill", _prefill(
+        _ptr(q_nope), qn_st, qn_sh, _ptr(q_pe), qp_st, qp_sh,
+        _ptr(kv), kv.stride(0), kv.stride(1), _ptr(pe), pe.stride(0), pe.stride(1),
+        _ptr(wkv_b), _ptr(indices), int(k_max), float(scale),
+        B, T, int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(out), o_st, o_sh, _ptr(lse), int(flags), _ptr(bitmap), words, _ptr(status), _stream(stream)))
+    return out
 
 
 def mla_combine(workspace, B: int, num_splits: int, o_latent, lse=None, status=None, stream=None):

@@ -125,8 +125,11 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
                    int32_t num_splits, void* workspace, size_t ws_bytes,
                    void* o_latent, float* lse,
                    uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
-                   float* scores_out, uint32_t* status_dev, mla::DecodeArgs* out) {
-  if (!q_abs || !q_pe || !kv || !pe || !seq_lens) return MLA_ERR_NULL_POINTER;
+                   float* scores_out, uint32_t* status_dev, mla::DecodeArgs* out,
+                   int32_t prefill_T = 0) {
+  // prefill_T > 0: prefill rows (B = prompts * prefill_T, token r % T of
+  // prompt r / T, causal lengths, no seq_lens, max_len = T).
+  if (!q_abs || !q_pe || !kv || !pe || (!seq_lens && prefill_T == 0)) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536 || k_max < 1 || max_len < 1) return MLA_ERR_BAD_DIM;
   if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
   if (!indices && k_max < max_len) return MLA_ERR_BAD_DIM;
@@ -174,6 +177,8 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
   a.chunk = (int32_t)chunk;
   a.B = B;
   a.S = num_splits;
+  a.causal = prefill_T > 0 ? 1 : 0;
+  a.rows_per_seq = prefill_T > 0 ? prefill_T : 1;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
@@ -255,6 +260,75 @@ int mla_sparse_decode_noalloc(const void* q_abs, const void* q_pe, int64_t q_pe_
   c.lse = lse;
   c.status = (flags & MLA_FLAG_VALIDATE) ? status_dev : nullptr;
   return hip_status(mla::launch_combine(c, stream));
+}
+
+size_t mla_prefill_workspace_bytes(int32_t B, int32_t T, int32_t num_splits) {
+  if (B < 1 || T < 1 || (int64_t)B * T > 65536) return 0;
+  const int32_t rows = B * T;
+  const size_t tile = (size_t)rows * MLA_HEADS * MLA_LATENT_DIM * sizeof(uint16_t);
+  if (num_splits == 1) return 2 * tile;
+  const size_t part = mla_workspace_bytes(rows, num_splits);
+  return part == 0 ? 0 : tile + part;
+}
+
+int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
+                       const void* q_pe, int64_t q_pe_st, int64_t q_pe_sh,
+                       const void* kv, int64_t kv_sb, int64_t kv_st,
+                       const void* pe, int64_t pe_sb, int64_t pe_st,
+                       const void* wkv_b, const int32_t* indices, int32_t k_max, float scale,
+                       int32_t B, int32_t T, int32_t num_splits, void* workspace, size_t ws_bytes,
+                       void* out, int64_t out_st, int64_t out_sh, float* lse,
+                       uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                       uint32_t* status_dev, void* stream) {
+  if (!q_nope || !wkv_b || !out || !workspace) return MLA_ERR_NULL_POINTER;
+  if (B < 1 || T < 1 || (int64_t)B * T > 65536) return MLA_ERR_BAD_DIM;
+  if (flags & MLA_FLAG_WRITE_SCORES) return MLA_ERR_BAD_DIM;  // not offered for prefill
+  if (!indices && k_max < T) return MLA_ERR_BAD_DIM;
+  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(out) || !aligned16(workspace) ||
+      !stride8(q_nope_st) || !stride8(q_nope_sh) || !stride8(out_st) || !stride8(out_sh))
+    return MLA_ERR_ALIGNMENT;
+  const int32_t rows = B * T;
+  if (num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
+  if (ws_bytes < mla_prefill_workspace_bytes(B, T, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (((int64_t)(rows - 1) * q_nope_st + MLA_NOPE_DIM) * 2 > (int64_t)UINT32_MAX) return MLA_ERR_RANGE;
+  const size_t tile = (size_t)rows * MLA_HEADS * MLA_LATENT_DIM * sizeof(uint16_t);
+  void* q_abs = workspace;
+  void* rest = static_cast<char*>(workspace) + tile;
+  mla::DecodeArgs d;
+  int st = prepare_decode(q_abs, q_pe, q_pe_st, q_pe_sh, kv, kv_sb, kv_st, pe, pe_sb, pe_st, nullptr, T,
+                          indices, k_max, scale, rows, num_splits, rest, ws_bytes - tile,
+                          num_splits == 1 ? rest : nullptr, lse, flags, attended_bitmap, bitmap_words, nullptr,
+                          status_dev, &d, T);
+  if (st != MLA_OK) return st;
+  if ((int64_t)num_splits * rows * MLA_HEADS * 8 > (int64_t)INT32_MAX) return MLA_ERR_RANGE;
+  mla::AbsorbArgs ab;
+  ab.q_nope = static_cast<const uint16_t*>(q_nope);
+  ab.q_sb = q_nope_st;
+  ab.q_sh = q_nope_sh;
+  ab.wkv_b = static_cast<const uint16_t*>(wkv_b);
+  ab.q_abs = static_cast<uint16_t*>(q_abs);
+  ab.B = rows;
+  st = hip_status(mla::launch_absorb(ab, stream));
+  if (st != MLA_OK) return st;
+  st = hip_status(mla::launch_decode(d, stream));
+  if (st != MLA_OK) return st;
+  mla::ValueUpArgs v = {};
+  v.wkv_b = static_cast<const uint16_t*>(wkv_b);
+  v.out = static_cast<uint16_t*>(out);
+  v.out_sb = out_st;
+  v.out_sh = out_sh;
+  v.B = rows;
+  if (num_splits == 1) {
+    v.o_latent = static_cast<const uint16_t*>(rest);
+  } else {
+    v.o_latent = nullptr;
+    v.part_o = d.part_o;
+    v.part_ml = d.part_ml;
+    v.S = num_splits;
+    v.lse = lse;
+    v.status = (flags & MLA_FLAG_VALIDATE) ? status_dev : nullptr;
+  }
+  return hip_status(mla::launch_value_up(v, stream));
 }
 
 int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,

@@ -36,8 +36,12 @@ struct DecodeArgs {
   int32_t max_len;
   int32_t k_max;
   int32_t chunk;            // index slots per split (multiple of 32)
-  int32_t B;
+  int32_t B;                // query rows (sequences in decode, B * T tokens in prefill)
   int32_t S;                // splits
+  int32_t causal;           // 0: decode (row b = sequence b, length seq_lens[b]);
+                            // 1: prefill, row r = token r % T of prompt r / T
+                            // (T = rows_per_seq), causal length r % T + 1, no seq_lens
+  int32_t rows_per_seq;
   float scale;              // softmax scale
   float scale_log2;         // softmax scale * log2(e)
   uint16_t* part_o;         // [S][B][128][512] bf16, unnormalised sum per split (S > 1)

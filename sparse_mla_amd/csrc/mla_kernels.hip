@@ -631,6 +631,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (unit >= units) return;
   const int b = unit / a.S, s = unit % a.S;
+  // Prefill: row b is query token b % T of prompt b / T, whose keys are the
+  // prompt's own positions (one cache per prompt), causally limited to the
+  // token's own position.  Decode: row b is sequence b.
+  const bool causal = a.causal != 0;
+  const int seq = causal ? b / a.rows_per_seq : b;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
@@ -701,7 +706,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // rows; a scalar load of the length would be waited on with the kernel
   // arguments, before anything else goes out).
   stage_query(7, 9);
-  dma4(buffer_rsrc(a.seq_lens + b, 4u), lds0 + (uint32_t)(kOffLen + 256 * wave), 4u * (uint32_t)lane);
+  // (In prefill mode there is no length array: a zero-byte range loads zeros.)
+  dma4(causal ? buffer_rsrc(a.q_abs, 0u) : buffer_rsrc(a.seq_lens + b, 4u),
+       lds0 + (uint32_t)(kOffLen + 256 * wave), 4u * (uint32_t)lane);
   if constexpr (!dense) {
     // 4 bytes per lane, so that the range check (nslot slots) is per slot.
     const i32x4 ri = buffer_rsrc(a.indices + (int64_t)b * a.k_max + s0, (uint32_t)nslot * 4u);
@@ -712,8 +719,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   stage_query(0, 7);
   asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
   read_query(28, 36);
-  const int Lb = __builtin_amdgcn_readfirstlane(
-      min(max(*(const volatile int LDS_AS*)(s3 + kOffLen + 256 * wave), 0), a.max_len));
+  const int Lb = causal ? min(b % a.rows_per_seq + 1, a.max_len)
+                        : __builtin_amdgcn_readfirstlane(
+                              min(max(*(const volatile int LDS_AS*)(s3 + kOffLen + 256 * wave), 0), a.max_len));
 
   // Stage this split's index slots as cache rows (-1 = masked).  The same
   // predicate decides validity, the attended bitmap and the device checks.
@@ -727,7 +735,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
         const int t = r[e];
         const bool ok = (i0 + e < nslot) && t >= 0 && t < Lb;
         if (validate && i0 + e < nslot) {
-          if (!ok && t != -1) atomicOr(a.status, 1u);
+          // Prefill: a key after the token (but inside the prompt) is
+          // removed by the causal mask, not an error.
+          if (!ok && t != -1 && !(causal && t >= Lb && t < a.max_len)) atomicOr(a.status, 1u);
           if (ok) {
             const uint32_t bit = 1u << (t & 31);
             const uint32_t old = atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), bit);
@@ -786,8 +796,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   };
 
   const uint32_t kv_rb = (uint32_t)(a.kv_st * 2), pe_rb = (uint32_t)(a.pe_st * 2);
-  const i32x4 rkv = buffer_rsrc(a.kv + (int64_t)b * a.kv_sb, (uint32_t)Lb * kv_rb);
-  const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)b * a.pe_sb, (uint32_t)Lb * pe_rb);
+  const i32x4 rkv = buffer_rsrc(a.kv + (int64_t)seq * a.kv_sb, (uint32_t)Lb * kv_rb);
+  const i32x4 rpe = buffer_rsrc(a.pe + (int64_t)seq * a.pe_sb, (uint32_t)Lb * pe_rb);
   // Gather block p into buffer p % 4: wave w moves keys 8 w .. 8 w + 7, all
   // 9 lines; lane l takes key 8 w + l / 8 and 16-byte position l % 8.
   struct Gather {

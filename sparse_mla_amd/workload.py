@@ -204,3 +204,61 @@ def output_proj_inputs(B: int, seed: int = 607, device="cpu"):
     x = _normal_bf16((B, 1, H, DV), _gen(device, seed), device)
     wo = _normal_bf16((7168, H * DV), _gen(device, seed + 1), device, std=(H * DV) ** -0.5)
     return x, wo
+
+
+@dataclass
+class Prefill:
+    """Inputs of a sparse prefill: B prompts of T tokens, each token with its
+    own selection of k positions of its prompt."""
+    B: int
+    T: int
+    q_nope: torch.Tensor              # bf16 [B, T, H, DN]
+    q_pe: torch.Tensor                # bf16 [B, T, H, DR]
+    cache: torch.Tensor               # bf16 [B, T, DQK] (latent | rotary) of the prompt positions
+    wkv_b: torch.Tensor               # bf16 [H*(DN+DV), DC]
+    indices: Optional[torch.Tensor]   # int32 [B, T, k] or None (every causal key)
+    scale: float = SOFTMAX_SCALE
+
+    @property
+    def kv(self) -> torch.Tensor:
+        return self.cache[..., :DC]
+
+    @property
+    def pe(self) -> torch.Tensor:
+        return self.cache[..., DC:]
+
+
+PREFILL_HEADLINE = dict(B=1, T=4096, k=2048)
+
+
+def make_prefill(B: int, T: int, k: Optional[int], seed: int = 6000, device="cpu", cache_device=None) -> Prefill:
+    """Seeded prefill inputs.  Token s selects, in shuffled order: while
+    s + 1 <= k, every position 0 .. s and k - s - 1 later positions of the
+    prompt (a top-k over causally masked index scores returns those too; the
+    causal mask removes them), -1 where the prompt is shorter than k;
+    otherwise the most recent min(512, k / 4) positions up to s and the rest
+    uniformly without replacement from the earlier ones.  k=None: no index
+    lists (every causal key).  Generators seeded seed + j as in make()."""
+    cdev = device if cache_device is None else cache_device
+    q_nope = _normal_bf16((B, T, H, DN), _gen(device, seed + 0), device)
+    q_pe = _normal_bf16((B, T, H, DR), _gen(device, seed + 1), device)
+    cache = _normal_bf16((B, T, DQK), _gen(cdev, seed + 2), cdev)
+    wkv_b = _normal_bf16((H * (DN + DV), DC), _gen(device, seed + 3), device, std=DC ** -0.5)
+    idx = None
+    if k is not None:
+        g = _gen("cpu", seed + 5)
+        idx = torch.full((B, T, k), -1, dtype=torch.int32)
+        recent = min(512, k // 4)
+        for b in range(B):
+            for s in range(T):
+                if s + 1 <= k:
+                    later = torch.randperm(T - s - 1, generator=g)[: k - s - 1] + s + 1
+                    r = torch.cat([torch.arange(s + 1), later])
+                else:
+                    win = torch.arange(s + 1 - recent, s + 1)
+                    rest = torch.randperm(s + 1 - recent, generator=g)[: k - recent]
+                    r = torch.cat([win, rest])
+                r = r[torch.randperm(r.numel(), generator=g)]
+                idx[b, s, : r.numel()] = r.to(torch.int32)
+        idx = idx.to(device)
+    return Prefill(B=B, T=T, q_nope=q_nope, q_pe=q_pe, cache=cache, wkv_b=wkv_b, indices=idx)
