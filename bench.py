@@ -297,7 +297,7 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     warm_ms = start.elapsed_time(end) / args.steps
-    last_set = sets[0]  # bufs.out holds the output of the warm pass's last step
+    last_set = sets[0]
     # Pass 2 (kernel time for the roofline): K decode launches back to back on
     # the same stream, cycling the input sets, bracketed by two HIP events.
     # An event pair around every launch would add ~3 us to each; back to
@@ -354,6 +354,31 @@ def main():
                  "kernel": "mla_output_proj", "weights": "bf16 [7168, 16384], 3 rotated copies"}
         log(f"output projection: {op_ms * 1e3:.2f} us ({oproj['achieved_GBps']:.0f} GB/s)")
         del ox, wos, oout
+    # fp8 weights: the same rotated steps with absorb and value-up reading the
+    # block-scaled fp8 weight directly (16.8 MB of codes per step instead of
+    # the 33.5 MB bf16 copy the step above reads), five trials, median.
+    fp8_direct = None
+    if spec.fp8:
+        fl = [mla.StepLauncher(bufs, w.q_nope, w.q_pe, w.kv, w.pe, None, w.seq_lens, w.max_len, w.indices, w.scale,
+                               w_fp8=w.wkv_b_fp8, w_scale=w.wkv_b_scale) for w in sets]
+        for i in range(min(args.warmup, 100)):
+            fl[i % R]()
+        ftr = []
+        for _ in range(5):
+            start.record(stream)
+            for i in range(args.steps):
+                fl[i % R]()
+            end.record(stream)
+            torch.cuda.synchronize()
+            ftr.append(start.elapsed_time(end) / args.steps)
+        fms = sorted(ftr)[2]
+        fbytes = sum(per_set[i % R][2] for i in range(args.steps)) / args.steps - WEIGHT_BYTES + WEIGHT_BYTES // 2 + 4096
+        fp8_direct = {"value": B / (fms * 1e-3), "unit": "queries/s", "us_per_step": fms * 1e3,
+                      "trials_us_per_step": [t * 1e3 for t in ftr],
+                      "step_roofline_frac": fbytes / (HBM_PEAK_GBS * 1e9) / (fms * 1e-3),
+                      "weight_bytes_per_step": WEIGHT_BYTES // 2 + 4096,
+                      "kernels": "mla_absorb_q_fp8 + mla_sparse_decode + mla_combine_value_up_fp8"}
+        log(f"fp8 weights read directly: {fms * 1e3:.2f} us/step")
     prefill = None
     if not args.no_prefill:
         prefill = prefill_pass(args, mla, workload, torch, stream)
@@ -373,7 +398,10 @@ def main():
     dec_tflops = dec_flops / (decode_ms * 1e-3) / 1e12
     step_roof_s = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (BF16_PEAK_TFLOPS * 1e12))
 
-    # Sampled parity of the last full step's output against the oracle.
+    # Sampled parity of one full step's output against the oracle: input set
+    # 0 once more, so that bufs.out is its output whatever ran last.
+    launchers[0]()
+    torch.cuda.synchronize()
     parity = None
     try:
         import numpy as np
@@ -465,6 +493,7 @@ def main():
                            else "mla_sparse_decode"},
         "output_proj": oproj,
         "prefill": prefill,
+        "fp8_weights_direct": fp8_direct,
         "attainable": attain,
         "parity_sampled_rel_err": parity,
         "cpu_baseline": cpu,

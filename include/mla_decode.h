@@ -281,6 +281,30 @@ int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
 int mla_dequant_wkv_b_fp8(const void* w_fp8, const float* scales, void* w_bf16, void* stream);
 
 /*
+ * Steps 1 and 4 reading the block-scaled fp8 weight directly instead of a
+ * bf16 copy ("Query-key similarity" page, code excerpt: a quantised wkv_b is
+ * dequantised through its block scale before the absorption).  Each call
+ * dequantises the slices it uses in registers, to exactly the values
+ * mla_dequant_wkv_b_fp8 writes (bf16 rounded to nearest even from the exact
+ * product e4m3(w[i][j]) * scale[i/128][j/128]), and so reads 16.8 MB of
+ * weight codes per step instead of 33.5 MB of bf16.
+ *   w_fp8    uint8 [32768][512] OCP E4M3FN codes, 16-byte aligned.
+ *   w_scale  fp32 [256][4] block scales, 4-byte aligned.
+ *   w_formed NULL, or bf16 [32768][512] (16-byte aligned): a test hook; the
+ *            call also writes the weights exactly as it formed them in
+ *            registers (the W_UK rows for absorb, the W_UV rows for value-up).
+ * The other arguments, the results and the errors are those of mla_absorb_q,
+ * mla_value_up and mla_combine_value_up.
+ */
+int mla_absorb_q_fp8(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh, const void* w_fp8,
+                     const float* w_scale, void* q_abs, int32_t B, void* w_formed, void* stream);
+int mla_value_up_fp8(const void* o_latent, const void* w_fp8, const float* w_scale, void* out,
+                     int64_t out_sb, int64_t out_sh, int32_t B, void* w_formed, void* stream);
+int mla_combine_value_up_fp8(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                             const void* w_fp8, const float* w_scale, void* out, int64_t out_sb, int64_t out_sh,
+                             float* lse, uint32_t* status_dev, void* stream);
+
+/*
  * Output projection, the step after the value-up ("Attention update" page,
  * mla-output excerpt: the head outputs are flattened per sequence and the
  * output linear layer maps them to the model width):

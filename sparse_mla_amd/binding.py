@@ -76,6 +76,10 @@ _value_up = _sig("mla_value_up", ctypes.c_int, [_p, _p, _p, _i64, _i64, _i32, _p
 _combine_value_up = _sig("mla_combine_value_up", ctypes.c_int,
                          [_p, _sz, _i32, _i32, _p, _p, _i64, _i64, _p, _p, _p])
 _dequant = _sig("mla_dequant_wkv_b_fp8", ctypes.c_int, [_p, _p, _p, _p])
+_absorb_fp8 = _sig("mla_absorb_q_fp8", ctypes.c_int, [_p, _i64, _i64, _p, _p, _p, _i32, _p, _p])
+_value_up_fp8 = _sig("mla_value_up_fp8", ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i32, _p, _p])
+_combine_value_up_fp8 = _sig("mla_combine_value_up_fp8", ctypes.c_int,
+                             [_p, _sz, _i32, _i32, _p, _p, _p, _i64, _i64, _p, _p, _p])
 _output_proj = _sig("mla_output_proj", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p])
 MODEL_DIM = 7168
 
@@ -368,6 +372,64 @@ def mla_output_proj(x: torch.Tensor, wo: torch.Tensor, out: Optional[torch.Tenso
     return out
 
 
+def _need_fp8_weight(w_fp8, w_scale):
+    _need(w_fp8, "w_fp8", torch.uint8, 2)
+    _need(w_scale, "w_scale", torch.float32, 2)
+    if tuple(w_fp8.shape) != (HEADS * (NOPE + VALUE), LATENT) or tuple(w_scale.shape) != (256, 4):
+        raise ValueError("w_fp8 must be [32768,512] and w_scale [256,4]")
+    if not (w_fp8.is_contiguous() and w_scale.is_contiguous()):
+        raise ValueError("w_fp8 and w_scale must be contiguous")
+
+
+def mla_absorb_q_fp8(q_nope, w_fp8, w_scale, q_abs=None, w_formed=None, stream=None):
+    """mla_absorb_q with the block-scaled fp8 weight read directly."""
+    _need(q_nope, "q_nope", torch.bfloat16)
+    _need_fp8_weight(w_fp8, w_scale)
+    B, H, sb, sh = _bsh(q_nope)
+    if H != HEADS or q_nope.shape[-1] != NOPE:
+        raise ValueError("shape mismatch with the fixed model dimensions")
+    if q_abs is None:
+        q_abs = torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=q_nope.device)
+    if tuple(q_abs.shape) != (B, HEADS, LATENT) or not q_abs.is_contiguous():
+        raise ValueError("q_abs must be a contiguous [B,128,512] tensor")
+    _check("mla_absorb_q_fp8", _absorb_fp8(_ptr(q_nope), sb, sh, _ptr(w_fp8), _ptr(w_scale), _ptr(q_abs), B,
+                                           _ptr(w_formed), _stream(stream)))
+    return q_abs
+
+
+def mla_value_up_fp8(o_latent, w_fp8, w_scale, out=None, w_formed=None, stream=None):
+    """mla_value_up with the block-scaled fp8 weight read directly."""
+    _need(o_latent, "o_latent", torch.bfloat16, 3)
+    _need_fp8_weight(w_fp8, w_scale)
+    B = o_latent.shape[0]
+    if not o_latent.is_contiguous() or tuple(o_latent.shape) != (B, HEADS, LATENT):
+        raise ValueError("o_latent must be a contiguous [B,128,512] tensor")
+    if out is None:
+        out = torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=o_latent.device)
+    Bo, Ho, sb, sh = _bsh(out)
+    if Bo != B or Ho != HEADS or out.shape[-1] != VALUE:
+        raise ValueError("out must be [B,1,128,128] or [B,128,128]")
+    _check("mla_value_up_fp8", _value_up_fp8(_ptr(o_latent), _ptr(w_fp8), _ptr(w_scale), _ptr(out), sb, sh, B,
+                                             _ptr(w_formed), _stream(stream)))
+    return out
+
+
+def mla_combine_value_up_fp8(workspace, B: int, num_splits: int, w_fp8, w_scale, out=None, lse=None, status=None,
+                             stream=None):
+    """mla_combine_value_up with the block-scaled fp8 weight read directly."""
+    _need_fp8_weight(w_fp8, w_scale)
+    if out is None:
+        out = torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=w_fp8.device)
+    Bo, Ho, sb, sh = _bsh(out)
+    if Bo != B or Ho != HEADS or out.shape[-1] != VALUE:
+        raise ValueError("out must be [B,1,128,128] or [B,128,128]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_combine_value_up_fp8", _combine_value_up_fp8(
+        _ptr(workspace), ws_bytes, B, num_splits, _ptr(w_fp8), _ptr(w_scale), _ptr(out), sb, sh, _ptr(lse),
+        _ptr(status), _stream(stream)))
+    return out
+
+
 def mla_dequant_wkv_b_fp8(w_fp8: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None,
                           stream=None) -> torch.Tensor:
     _need(w_fp8, "w_fp8", torch.uint8, 2)
@@ -442,9 +504,17 @@ class StepLauncher:
     raises on a non-zero status."""
 
     def __init__(self, bufs: DecodeBuffers, q_nope, q_pe, kv, pe, wkv_b, seq_lens, max_len, indices, scale,
-                 stream=None):
+                 stream=None, w_fp8=None, w_scale=None):
+        """With w_fp8 and w_scale (and wkv_b None) the step reads the
+        block-scaled fp8 weight directly (mla_absorb_q_fp8,
+        mla_combine_value_up_fp8 / mla_value_up_fp8)."""
+        fp8 = w_fp8 is not None
+        if fp8:
+            _need_fp8_weight(w_fp8, w_scale)
+            wkv_b = w_fp8
         for t, name, dt in ((q_nope, "q_nope", torch.bfloat16), (q_pe, "q_pe", torch.bfloat16),
-                            (kv, "kv", torch.bfloat16), (pe, "pe", torch.bfloat16), (wkv_b, "wkv_b", torch.bfloat16),
+                            (kv, "kv", torch.bfloat16), (pe, "pe", torch.bfloat16),
+                            (wkv_b, "wkv_b", torch.uint8 if fp8 else torch.bfloat16),
                             (seq_lens, "seq_lens", torch.int32)):
             _need(t, name, dt)
         B = bufs.B
@@ -465,8 +535,11 @@ class StepLauncher:
         _, _, o_sb, o_sh = _bsh(bufs.out)
         ws_bytes = 0 if bufs.workspace is None else bufs.workspace.numel()
         k_max = bufs.k_max if indices is None else indices.shape[1]
+        absorb = ((_absorb_fp8, "mla_absorb_q_fp8", (_ptr(q_nope), qn_sb, qn_sh, _ptr(w_fp8), _ptr(w_scale),
+                                                     _ptr(bufs.q_abs), B, None, st)) if fp8 else
+                  (_absorb, "mla_absorb_q", (_ptr(q_nope), qn_sb, qn_sh, _ptr(wkv_b), _ptr(bufs.q_abs), B, st)))
         self._calls = [
-            (_absorb, "mla_absorb_q", (_ptr(q_nope), qn_sb, qn_sh, _ptr(wkv_b), _ptr(bufs.q_abs), B, st)),
+            absorb,
             (_decode, "mla_sparse_decode", (
                 _ptr(bufs.q_abs), _ptr(q_pe), qp_sb, qp_sh,
                 _ptr(kv), kv.stride(0), kv.stride(1), _ptr(pe), pe.stride(0), pe.stride(1),
@@ -474,10 +547,17 @@ class StepLauncher:
                 bufs.num_splits, _ptr(bufs.workspace), ws_bytes, _ptr(bufs.o_latent), _ptr(bufs.lse),
                 0, None, 0, None, None, st)),
         ]
-        if bufs.num_splits > 1:
+        if bufs.num_splits > 1 and fp8:
+            self._calls.append((_combine_value_up_fp8, "mla_combine_value_up_fp8", (
+                _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits, _ptr(w_fp8), _ptr(w_scale), _ptr(bufs.out), o_sb,
+                o_sh, _ptr(bufs.lse), None, st)))
+        elif bufs.num_splits > 1:
             self._calls.append((_combine_value_up, "mla_combine_value_up", (
                 _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits, _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh,
                 _ptr(bufs.lse), None, st)))
+        elif fp8:
+            self._calls.append((_value_up_fp8, "mla_value_up_fp8", (
+                _ptr(bufs.o_latent), _ptr(w_fp8), _ptr(w_scale), _ptr(bufs.out), o_sb, o_sh, B, None, st)))
         else:
             self._calls.append((_value_up, "mla_value_up", (
                 _ptr(bufs.o_latent), _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh, B, st)))

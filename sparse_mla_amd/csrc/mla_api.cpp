@@ -91,24 +91,59 @@ int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus, int32_t* 
   return MLA_OK;
 }
 
-int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
-                 const void* wkv_b, void* q_abs, int32_t B, void* stream) {
-  if (!q_nope || !wkv_b || !q_abs) return MLA_ERR_NULL_POINTER;
+}  // extern "C"
+
+namespace {
+
+int absorb_impl(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh, const void* wkv_b,
+                const mla::Fp8Weight& fp8, void* q_abs, int32_t B, void* stream) {
+  if (!q_nope || !q_abs || (!wkv_b && !fp8.w_fp8)) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536) return MLA_ERR_BAD_DIM;
-  if (!aligned16(q_nope) || !aligned16(wkv_b) || !aligned16(q_abs) || !stride8(q_nope_sb) ||
-      !stride8(q_nope_sh))
+  if (!aligned16(q_nope) || !aligned16(q_abs) || !stride8(q_nope_sb) || !stride8(q_nope_sh) ||
+      (wkv_b && !aligned16(wkv_b)))
     return MLA_ERR_ALIGNMENT;
   // One head's rows are read with 32-bit byte offsets.
   if (q_nope_sb < 0 || q_nope_sh < 0 || ((int64_t)(B - 1) * q_nope_sb + MLA_NOPE_DIM) * 2 > (int64_t)UINT32_MAX)
     return MLA_ERR_RANGE;
-  mla::AbsorbArgs a;
+  mla::AbsorbArgs a = {};
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_sb = q_nope_sb;
   a.q_sh = q_nope_sh;
   a.wkv_b = static_cast<const uint16_t*>(wkv_b);
   a.q_abs = static_cast<uint16_t*>(q_abs);
   a.B = B;
+  a.fp8 = fp8;
   return hip_status(mla::launch_absorb(a, stream));
+}
+
+// The fp8 weight arguments: codes 16-byte aligned, scales 4-byte aligned,
+// the optional formed-weight output 16-byte aligned.
+int fp8_weight(const void* w_fp8, const float* w_scale, void* w_formed, mla::Fp8Weight* out) {
+  if (!w_fp8 || !w_scale) return MLA_ERR_NULL_POINTER;
+  if (!aligned16(w_fp8) || (reinterpret_cast<uintptr_t>(w_scale) & 3u) || (w_formed && !aligned16(w_formed)))
+    return MLA_ERR_ALIGNMENT;
+  out->w_fp8 = static_cast<const uint8_t*>(w_fp8);
+  out->w_scale = w_scale;
+  out->w_formed = static_cast<uint16_t*>(w_formed);
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
+                 const void* wkv_b, void* q_abs, int32_t B, void* stream) {
+  if (!wkv_b) return MLA_ERR_NULL_POINTER;
+  return absorb_impl(q_nope, q_nope_sb, q_nope_sh, wkv_b, mla::Fp8Weight{}, q_abs, B, stream);
+}
+
+int mla_absorb_q_fp8(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh, const void* w_fp8,
+                     const float* w_scale, void* q_abs, int32_t B, void* w_formed, void* stream) {
+  mla::Fp8Weight f;
+  const int st = fp8_weight(w_fp8, w_scale, w_formed, &f);
+  if (st != MLA_OK) return st;
+  return absorb_impl(q_nope, q_nope_sb, q_nope_sh, nullptr, f, q_abs, B, stream);
 }
 
 }  // extern "C"
@@ -301,7 +336,7 @@ int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
                           status_dev, &d, T);
   if (st != MLA_OK) return st;
   if ((int64_t)num_splits * rows * MLA_HEADS * 8 > (int64_t)INT32_MAX) return MLA_ERR_RANGE;
-  mla::AbsorbArgs ab;
+  mla::AbsorbArgs ab = {};
   ab.q_nope = static_cast<const uint16_t*>(q_nope);
   ab.q_sb = q_nope_st;
   ab.q_sh = q_nope_sh;
@@ -350,11 +385,15 @@ int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_s
   return hip_status(mla::launch_combine(a, stream));
 }
 
-int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
-                 int64_t out_sb, int64_t out_sh, int32_t B, void* stream) {
-  if (!o_latent || !wkv_b || !out) return MLA_ERR_NULL_POINTER;
+}  // extern "C"
+
+namespace {
+
+int value_up_impl(const void* o_latent, const void* wkv_b, const mla::Fp8Weight& fp8, void* out,
+                  int64_t out_sb, int64_t out_sh, int32_t B, void* stream) {
+  if (!o_latent || !out || (!wkv_b && !fp8.w_fp8)) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536) return MLA_ERR_BAD_DIM;
-  if (!aligned16(o_latent) || !aligned16(wkv_b) || !aligned16(out) || !stride8(out_sb) ||
+  if (!aligned16(o_latent) || (wkv_b && !aligned16(wkv_b)) || !aligned16(out) || !stride8(out_sb) ||
       !stride8(out_sh))
     return MLA_ERR_ALIGNMENT;
   mla::ValueUpArgs a = {};
@@ -364,7 +403,53 @@ int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
   a.out_sb = out_sb;
   a.out_sh = out_sh;
   a.B = B;
+  a.fp8 = fp8;
   return hip_status(mla::launch_value_up(a, stream));
+}
+
+int combine_value_up_impl(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                          const void* wkv_b, const mla::Fp8Weight& fp8, void* out, int64_t out_sb, int64_t out_sh,
+                          float* lse, uint32_t* status_dev, void* stream) {
+  if (B < 1 || B > 65536 || num_splits < 2 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
+  if (!workspace || !out || (!wkv_b && !fp8.w_fp8)) return MLA_ERR_NULL_POINTER;
+  if (!aligned16(workspace) || (wkv_b && !aligned16(wkv_b)) || !aligned16(out) || !stride8(out_sb) ||
+      !stride8(out_sh))
+    return MLA_ERR_ALIGNMENT;
+  if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  if (units * 8 > (size_t)INT32_MAX) return MLA_ERR_RANGE;  // (max, sum) addressed with 32-bit offsets
+  mla::ValueUpArgs a = {};
+  a.o_latent = nullptr;
+  a.wkv_b = static_cast<const uint16_t*>(wkv_b);
+  a.out = static_cast<uint16_t*>(out);
+  a.out_sb = out_sb;
+  a.out_sh = out_sh;
+  a.B = B;
+  a.part_o = static_cast<const uint16_t*>(workspace);
+  a.part_ml = reinterpret_cast<const float*>(static_cast<const uint16_t*>(workspace) + units * MLA_LATENT_DIM);
+  a.S = num_splits;
+  a.lse = lse;
+  a.status = status_dev;
+  a.fp8 = fp8;
+  return hip_status(mla::launch_value_up(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
+                 int64_t out_sb, int64_t out_sh, int32_t B, void* stream) {
+  if (!wkv_b) return MLA_ERR_NULL_POINTER;
+  return value_up_impl(o_latent, wkv_b, mla::Fp8Weight{}, out, out_sb, out_sh, B, stream);
+}
+
+int mla_value_up_fp8(const void* o_latent, const void* w_fp8, const float* w_scale, void* out,
+                     int64_t out_sb, int64_t out_sh, int32_t B, void* w_formed, void* stream) {
+  mla::Fp8Weight f;
+  const int st = fp8_weight(w_fp8, w_scale, w_formed, &f);
+  if (st != MLA_OK) return st;
+  return value_up_impl(o_latent, nullptr, f, out, out_sb, out_sh, B, stream);
 }
 
 int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
@@ -390,26 +475,19 @@ int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int6
 int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
                          const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh, float* lse,
                          uint32_t* status_dev, void* stream) {
-  if (B < 1 || B > 65536 || num_splits < 2 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
-  if (!workspace || !wkv_b || !out) return MLA_ERR_NULL_POINTER;
-  if (!aligned16(workspace) || !aligned16(wkv_b) || !aligned16(out) || !stride8(out_sb) || !stride8(out_sh))
-    return MLA_ERR_ALIGNMENT;
-  if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
-  if (units * 8 > (size_t)INT32_MAX) return MLA_ERR_RANGE;  // (max, sum) addressed with 32-bit offsets
-  mla::ValueUpArgs a = {};
-  a.o_latent = nullptr;
-  a.wkv_b = static_cast<const uint16_t*>(wkv_b);
-  a.out = static_cast<uint16_t*>(out);
-  a.out_sb = out_sb;
-  a.out_sh = out_sh;
-  a.B = B;
-  a.part_o = static_cast<const uint16_t*>(workspace);
-  a.part_ml = reinterpret_cast<const float*>(static_cast<const uint16_t*>(workspace) + units * MLA_LATENT_DIM);
-  a.S = num_splits;
-  a.lse = lse;
-  a.status = status_dev;
-  return hip_status(mla::launch_value_up(a, stream));
+  if (!wkv_b) return MLA_ERR_NULL_POINTER;
+  return combine_value_up_impl(workspace, ws_bytes, B, num_splits, wkv_b, mla::Fp8Weight{}, out, out_sb, out_sh,
+                               lse, status_dev, stream);
+}
+
+int mla_combine_value_up_fp8(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                             const void* w_fp8, const float* w_scale, void* out, int64_t out_sb, int64_t out_sh,
+                             float* lse, uint32_t* status_dev, void* stream) {
+  mla::Fp8Weight f;
+  const int st = fp8_weight(w_fp8, w_scale, nullptr, &f);
+  if (st != MLA_OK) return st;
+  return combine_value_up_impl(workspace, ws_bytes, B, num_splits, nullptr, f, out, out_sb, out_sh, lse, status_dev,
+                               stream);
 }
 
 int mla_dequant_wkv_b_fp8(const void* w_fp8, const float* scales, void* w_bf16, void* stream) {

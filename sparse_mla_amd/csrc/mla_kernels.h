@@ -15,12 +15,21 @@ constexpr int kValue = 128;
 constexpr int kRowsPerHead = kNope + kValue;  // 256 rows of wkv_b per head
 constexpr int kIdxCap = 1024;                  // index slots staged per split
 
+// Block-scaled fp8 weight (read instead of wkv_b when w_fp8 != NULL): E4M3FN
+// codes [32768][512] and fp32 scales [256][4], one per 128 x 128 block.
+struct Fp8Weight {
+  const uint8_t* w_fp8;
+  const float* w_scale;
+  uint16_t* w_formed;       // test hook: the bf16 weights as formed in registers (may be NULL)
+};
+
 struct AbsorbArgs {
   const uint16_t* q_nope;
   int64_t q_sb, q_sh;
   const uint16_t* wkv_b;
   uint16_t* q_abs;
   int32_t B;
+  Fp8Weight fp8;
 };
 
 struct DecodeArgs {
@@ -76,6 +85,7 @@ struct ValueUpArgs {
   int32_t S;
   float* lse;
   uint32_t* status;
+  Fp8Weight fp8;
 };
 
 struct DequantArgs {

@@ -157,6 +157,70 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 }
 
 // ---------------------------------------------------------------------------
+// fp8 dequantisation: E4M3FN from its definition (sign, 4 exponent bits with
+// bias 7, 3 mantissa bits; exponent 0 is subnormal, m/8 * 2^-6; 0x7F / 0xFF
+// are NaN).  The product with the fp32 block scale is rounded to bf16 from
+// its exact value: p = fl(v * s) plus the exact residual fma(v, s, -p)
+// decide the ties that fl() can create.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  float v;
+  if (e == 0u) v = (float)m * 0x1p-9f;
+  else if (e == 15u && m == 7u) v = __builtin_nanf("");
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (code & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_exact(float p, float err) {
+  const uint32_t u = __float_as_uint(p);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  const uint32_t lower = u & 0xffffu, hi = u >> 16;
+  bool up;
+  if (lower > 0x8000u) up = true;
+  else if (lower < 0x8000u) up = false;
+  else if (err == 0.f) up = (hi & 1u) != 0u;
+  else up = (err > 0.f) == (p > 0.f);   // the exact value lies beyond the tie
+  return hi + (up ? 1u : 0u);
+}
+
+// Two fp8 codes (bytes 0-1 of `word`, or 2-3 with HI) times the block
+// scale, rounded to bf16, packed.  The hardware conversion decodes the codes
+// exactly.  Rounding the fp32 product fl(v * s) to bf16 equals rounding the
+// exact product except where fl(v * s) sits exactly on a bf16 tie (low 16
+// bits 0x8000) with a nonzero residual: EXACT settles every pair by the exact
+// rule above; otherwise the packed round-to-nearest-even conversion is used,
+// for blocks that block_has_ties() clears.  A NaN code gives a bf16 NaN.
+template <bool HI, bool EXACT>
+__device__ __forceinline__ uint32_t dq_pair(uint32_t word, float s) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+  const float p0 = v[0] * s, p1 = v[1] * s;
+  if constexpr (EXACT)
+    return bf16_rne_exact(p0, __builtin_fmaf(v[0], s, -p0)) | (bf16_rne_exact(p1, __builtin_fmaf(v[1], s, -p1)) << 16);
+  return pack2(p0, p1);
+}
+// Eight codes (two words) -> eight bf16 values as an MFMA operand.
+template <bool EXACT>
+__device__ __forceinline__ bf16x8 dq8(uint2 codes, float s) {
+  const uint4 w = uint4{dq_pair<false, EXACT>(codes.x, s), dq_pair<true, EXACT>(codes.x, s),
+                        dq_pair<false, EXACT>(codes.y, s), dq_pair<true, EXACT>(codes.y, s)};
+  return __builtin_bit_cast(bf16x8, w);
+}
+// Whether some code, times the block scale s, has its fp32 product on a bf16
+// tie with a nonzero residual -- the only products whose bf16 rounding needs
+// the exact rule.  Wave-uniform: each lane tests four of the 256 codes.
+__device__ __forceinline__ bool block_has_ties(float s, int lane) {
+  bool t = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float v = __builtin_amdgcn_cvt_f32_fp8(lane + 64 * k, 0);
+    const float p = v * s;
+    t |= ((__float_as_uint(p) & 0xffffu) == 0x8000u) && (__builtin_fmaf(v, s, -p) != 0.f);
+  }
+  return __builtin_amdgcn_ballot_w64(t) != 0;
+}
+
+// ---------------------------------------------------------------------------
 // absorb: q_abs[b][h][c] = sum_d q_nope[b][h][d] W_UK,h[d][c]
 // Workgroup = (head, 256-column half): 256 workgroups, each streaming its
 // 64 KB slab of W_UK once.  W_UK is stored [d][c] (c contiguous) while d is
@@ -178,6 +242,12 @@ constexpr int kAbsQ = 32 * 1024;             // one quarter of the slab
 constexpr int kAbsQTile = 2 * 32 * 128;      // one 32-row query tile (8 KB)
 constexpr int kAbsLds = 2 * kAbsQ + 4 * kAbsQTile;
 
+// With FP8 the slab is read as block-scaled fp8 codes (32 KB per half, one
+// scale per quarter: its 128 rows and 128 columns are one scale block) by
+// ordinary 16-byte loads into registers and dequantised to bf16 straight into
+// the same swizzled LDS layout; the loads of both quarters go out first and
+// each quarter is converted when its products need it.
+template <bool FP8>
 __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
   __shared__ __attribute__((aligned(1024))) char wt[kAbsLds];
   const int h = blockIdx.x & (kHeads - 1);
@@ -202,6 +272,56 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
       dma16(rw, lds0 + (uint32_t)(m * 128 + 8 * rg) * 128u, d * (uint32_t)(kLatent * 2) + (uint32_t)m * 128u + q * 16u);
     }
   };
+  // fp8 slab, quarter Q: thread t takes rows d = (t + 256 k) / 8 and 16
+  // columns 16 g, g = t % 8, of the quarter (4 loads of 16 codes).
+  auto load_slab8 = [&](int Q, uint4 (&raw)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + 256 * k, d = i >> 3, g = i & 7;
+      raw[k] = *reinterpret_cast<const uint4*>(a.fp8.w_fp8 + ((size_t)h * kRowsPerHead + d) * kLatent + ch * 256 +
+                                               128 * Q + 16 * g);
+    }
+  };
+  // The two quarters' scales and whether either needs the exact rounding
+  // rule (read first: nothing else is in flight yet).
+  float qsc[2] = {0.f, 0.f};
+  bool qtie[2] = {false, false};
+  if constexpr (FP8) {
+#pragma unroll
+    for (int Q = 0; Q < 2; ++Q) {
+      qsc[Q] = a.fp8.w_scale[(2 * h) * (kLatent / 128) + 2 * ch + Q];
+      qtie[Q] = block_has_ties(qsc[Q], lane);
+    }
+  }
+  auto store_slab8 = [&](int Q, const uint4 (&raw)[4]) __attribute__((always_inline)) {
+    const float sc = qsc[Q];
+    const bool exact = qtie[Q];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + 256 * k, d = i >> 3, g = i & 7;
+      bf16x8 lo, hi;
+      if (__builtin_expect(exact, 0)) {
+        lo = dq8<true>(uint2{raw[k].x, raw[k].y}, sc);
+        hi = dq8<true>(uint2{raw[k].z, raw[k].w}, sc);
+      } else {
+        lo = dq8<false>(uint2{raw[k].x, raw[k].y}, sc);
+        hi = dq8<false>(uint2{raw[k].z, raw[k].w}, sc);
+      }
+      const uint32_t m = (uint32_t)(2 * Q + (g >> 2));
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t q = (uint32_t)(2 * (g & 3) + c);
+        *(bf16x8 LDS_AS*)((char LDS_AS*)wt + (m * 128u + (uint32_t)d) * 128u + ((q ^ (2u * ((uint32_t)d & 3u))) * 16u)) =
+            c ? hi : lo;
+      }
+      if (a.fp8.w_formed != nullptr) {
+        uint16_t* f = a.fp8.w_formed + ((size_t)h * kRowsPerHead + d) * kLatent + ch * 256 + 128 * Q + 16 * g;
+        *reinterpret_cast<bf16x8*>(f) = lo;
+        *reinterpret_cast<bf16x8*>(f + 8) = hi;
+      }
+    }
+  };
+  uint4 raw0[4], raw1[4];
   // Query tiles bt0 .. bt0 + 3 (those that exist): 8 instructions per tile,
   // 2 per wave; rows past B load row B - 1 (their columns are never stored).
   const int nbt = (a.B + 31) / 32;
@@ -280,10 +400,18 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
     const int nq = min(4, nbt - bt0);
     if (bt0 == 0) {
       // Quarter 0 of the slab, the first query tiles, quarter 1 of the slab.
-      stage_slab(0);
-      stage_q(0);
-      stage_slab(1);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      if constexpr (FP8) {
+        load_slab8(0, raw0);
+        stage_q(0);
+        load_slab8(1, raw1);
+        store_slab8(0, raw0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        stage_slab(0);
+        stage_q(0);
+        stage_slab(1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      }
     } else {
       // Every wave is done with the previous query tiles (their reads
       // completed before its last copy-out, which precedes the barrier of
@@ -311,6 +439,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
       out_tile(0, bt0 + u, af0, qb[u]);
     }
     if (bt0 == 0) {
+      if constexpr (FP8) store_slab8(1, raw1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       read_slab(1, af1);
@@ -341,7 +470,10 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kOtRow = 1040;  // bytes per latent row in LDS (512 bf16 + 16 pad)
 
-template <bool FUSED, int ROWS, int SPP>
+// With FP8, W_UV,h is read as block-scaled fp8 codes (8 per lane per K-step,
+// in the same issue slots as the bf16 loads) and dequantised to bf16 in
+// registers before the products; K-step st lies in scale block column st / 8.
+template <bool FUSED, int ROWS, int SPP, bool FP8>
 __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   __shared__ __attribute__((aligned(1024))) char slots[SPP * ROWS * kOtRow];
   __shared__ float wtab[ROWS * 64];  // merge weights: per wave, row, split
@@ -364,6 +496,17 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 
   const int S = FUSED ? a.S : 1;
   const int64_t sstride = (int64_t)a.B * kHeads;  // rows per split
+  // fp8: the four scale blocks of W_UV,h (row block 2h + 1) and whether each
+  // needs the exact rounding rule, settled before anything else is in flight.
+  float wsc[4] = {0.f, 0.f, 0.f, 0.f};
+  bool wtie[4] = {false, false, false, false};
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wsc[j] = a.fp8.w_scale[(2 * h + 1) * (kLatent / 128) + j];
+      wtie[j] = block_has_ties(wsc[j], lane);
+    }
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(char LDS_AS*)slots;
   const int n = min(RPW, max(0, nrows - r0));  // rows of this wave that exist
   // The wave's own LDS slots hold kCap rows; a pass stages splits
@@ -434,8 +577,15 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   const int g0 = n > 0 ? ps0 * n : 0;  // partial-row loads of the first pass
   wait_vm_le(g0);
 
-  const uint16_t* w = a.wkv_b + ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
+  const size_t wrow = ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
+  const uint16_t* w = a.wkv_b + wrow;
+  const uint8_t* w8 = a.fp8.w_fp8 + wrow;
   bf16x8 wf[32];
+  uint2 wr[FP8 ? 32 : 1];
+  auto load_w = [&](int st) __attribute__((always_inline)) {
+    if constexpr (FP8) wr[st] = *reinterpret_cast<const uint2*>(w8 + 16 * st);
+    else wf[st] = ld8(w + 16 * st);
+  };
 
   // Merge weights g_s = 2^(m_s - M) / L of the row, from a group max and a
   // group sum over the row's G lanes, into a per-wave table (an all -inf row
@@ -489,7 +639,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 #pragma unroll
         for (int u = 0; u < kLoadsPerStep; ++u) {
           const int st = (sc * RPW + j) * kLoadsPerStep + u;
-          wf[st] = ld8(w + 16 * st);
+          load_w(st);
         }
         if (sc < ps0) merge_step(0, sc, j);
         __builtin_amdgcn_sched_barrier(0);
@@ -514,7 +664,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
     // kCap / n splits.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int st = 0; st < 32; ++st) wf[st] = ld8(w + 16 * st);
+    for (int st = 0; st < 32; ++st) load_w(st);
     if (n > 0) {
       for (int c0 = 0; c0 < S;) {
         const int ps = pass_splits(c0);
@@ -542,6 +692,22 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   }
   __syncthreads();
 
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (__builtin_expect(wtie[j], 0)) {
+#pragma unroll
+        for (int st = 8 * j; st < 8 * j + 8; ++st) wf[st] = dq8<true>(wr[st], wsc[j]);
+      } else {
+#pragma unroll
+        for (int st = 8 * j; st < 8 * j + 8; ++st) wf[st] = dq8<false>(wr[st], wsc[j]);
+      }
+    }
+    if (a.fp8.w_formed != nullptr && b0 == 0) {
+#pragma unroll
+      for (int st = 0; st < 32; ++st) *reinterpret_cast<bf16x8*>(a.fp8.w_formed + wrow + 16 * st) = wf[st];
+    }
+  }
   // N = 32 tile rows; with ROWS = 16 the upper 16 columns are not written.
   f32x16 acc = {};
   const char LDS_AS* ol = (const char LDS_AS*)slots + (lane & 31) * kOtRow + 16 * hh;
@@ -1248,33 +1414,9 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
 }
 
 // ---------------------------------------------------------------------------
-// fp8 dequantisation (one-time set-up).  E4M3FN from its definition: sign,
-// 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is subnormal
-// (m/8 * 2^-6); 0x7F / 0xFF are NaN.  The product with the fp32 block scale
-// is rounded to bf16 from its exact value: p = fl(v * s) plus the exact
-// residual fma(v, s, -p) decide the rare ties that fl() creates.
+// fp8 dequantisation (one-time set-up): the whole weight, with the helpers
+// above.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_value(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  float v;
-  if (e == 0u) v = (float)m * 0x1p-9f;
-  else if (e == 15u && m == 7u) v = __builtin_nanf("");
-  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (code & 0x80u) ? -v : v;
-}
-
-__device__ __forceinline__ uint32_t bf16_rne_exact(float p, float err) {
-  const uint32_t u = __float_as_uint(p);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  const uint32_t lower = u & 0xffffu, hi = u >> 16;
-  bool up;
-  if (lower > 0x8000u) up = true;
-  else if (lower < 0x8000u) up = false;
-  else if (err == 0.f) up = (hi & 1u) != 0u;
-  else up = (err > 0.f) == (p > 0.f);   // the exact value lies beyond the tie
-  return hi + (up ? 1u : 0u);
-}
-
 __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
   const int row = (int)(i / kLatent), col = (int)(i % kLatent);
@@ -1301,7 +1443,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 }  // namespace
 
 int launch_absorb(const AbsorbArgs& a, void* stream) {
-  hipLaunchKernelGGL(absorb_kernel, dim3(kHeads * 2), dim3(256), 0, (hipStream_t)stream, a);
+  if (a.fp8.w_fp8 != nullptr)
+    hipLaunchKernelGGL(absorb_kernel<true>, dim3(kHeads * 2), dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(absorb_kernel<false>, dim3(kHeads * 2), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
@@ -1329,6 +1474,22 @@ int launch_combine(const CombineArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
+template <bool FP8>
+static void launch_value_up_t(const ValueUpArgs& a, dim3 grid, bool small, bool two, hipStream_t st) {
+  if (a.o_latent == nullptr) {
+    if (small) {
+      if (two) hipLaunchKernelGGL((value_up_kernel<true, 16, 2, FP8>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((value_up_kernel<true, 16, 4, FP8>), grid, dim3(256), 0, st, a);
+    } else {
+      if (two) hipLaunchKernelGGL((value_up_kernel<true, 32, 2, FP8>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((value_up_kernel<true, 32, 4, FP8>), grid, dim3(256), 0, st, a);
+    }
+  } else {
+    if (small) hipLaunchKernelGGL((value_up_kernel<false, 16, 2, FP8>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((value_up_kernel<false, 32, 2, FP8>), grid, dim3(256), 0, st, a);
+  }
+}
+
 int launch_value_up(const ValueUpArgs& a, void* stream) {
   // 32-row tiles, or 16 when that is what it takes to give every CU a tile.
   // Two splits staged per pass when there are at most two (half the LDS, so
@@ -1339,18 +1500,8 @@ int launch_value_up(const ValueUpArgs& a, void* stream) {
   const int units = kHeads * ((a.B + rows - 1) / rows);
   const dim3 grid(8 * ((units + 7) / 8));
   const hipStream_t st = (hipStream_t)stream;
-  if (a.o_latent == nullptr) {
-    if (small) {
-      if (two) hipLaunchKernelGGL((value_up_kernel<true, 16, 2>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((value_up_kernel<true, 16, 4>), grid, dim3(256), 0, st, a);
-    } else {
-      if (two) hipLaunchKernelGGL((value_up_kernel<true, 32, 2>), grid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((value_up_kernel<true, 32, 4>), grid, dim3(256), 0, st, a);
-    }
-  } else {
-    if (small) hipLaunchKernelGGL((value_up_kernel<false, 16, 2>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((value_up_kernel<false, 32, 2>), grid, dim3(256), 0, st, a);
-  }
+  if (a.fp8.w_fp8 != nullptr) launch_value_up_t<true>(a, grid, small, two, st);
+  else launch_value_up_t<false>(a, grid, small, two, st);
   return (int)hipGetLastError();
 }
 
