@@ -93,6 +93,7 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak microbenchmarks")
     ap.add_argument("--no-output-proj", action="store_true", help="skip timing the output projection")
     ap.add_argument("--no-prefill", action="store_true", help="skip timing the sparse prefill")
+    ap.add_argument("--no-heads", action="store_true", help="skip timing the head-sharded steps")
     ap.add_argument("--cpu-sample", type=int, default=None, help="sequences in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
@@ -379,6 +380,35 @@ def main():
                       "weight_bytes_per_step": WEIGHT_BYTES // 2 + 4096,
                       "kernels": "mla_absorb_q_fp8 + mla_sparse_decode + mla_combine_value_up_fp8"}
         log(f"fp8 weights read directly: {fms * 1e3:.2f} us/step")
+    # Head-sharded step (one GPU's share of 16, 32 or 64 heads, with its rows
+    # of wkv_b): the same rotated inputs, five trials of K steps, median.
+    heads_sharded = None
+    if not args.no_heads and not spec.fp8:
+        heads_sharded = {}
+        for H in (64, 32, 16):
+            hb = mla.DecodeBuffers.allocate(B, k_max, dense, num_splits=bufs.num_splits, heads=H)
+            shards = [(w.q_nope[:, :, :H].contiguous(), w.q_pe[:, :, :H].contiguous(),
+                       w.wkv_b[: H * 256].contiguous()) for w in sets]
+            hl = [mla.StepLauncher(hb, qn, qp, w.kv, w.pe, wk, w.seq_lens, w.max_len, w.indices, w.scale)
+                  for w, (qn, qp, wk) in zip(sets, shards)]
+            for i in range(min(args.warmup, 100)):
+                hl[i % R]()
+            htr = []
+            for _ in range(5):
+                start.record(stream)
+                for i in range(args.steps):
+                    hl[i % R]()
+                end.record(stream)
+                torch.cuda.synchronize()
+                htr.append(start.elapsed_time(end) / args.steps)
+            hms = sorted(htr)[2]
+            hbytes = (sum(per_set[i % R][1] for i in range(args.steps)) / args.steps + WEIGHT_BYTES * H // 128 +
+                      B * (Q_BYTES_PER_QUERY + O_BYTES_PER_QUERY) * H // 128)
+            heads_sharded[str(H)] = {"us_per_step": hms * 1e3, "queries_per_s": B / (hms * 1e-3),
+                                     "trials_us_per_step": [t * 1e3 for t in htr],
+                                     "step_roofline_frac": hbytes / (HBM_PEAK_GBS * 1e9) / (hms * 1e-3)}
+            log(f"heads {H}: {hms * 1e3:.2f} us/step")
+            del hl, shards, hb
     prefill = None
     if not args.no_prefill:
         prefill = prefill_pass(args, mla, workload, torch, stream)
@@ -494,6 +524,7 @@ def main():
         "output_proj": oproj,
         "prefill": prefill,
         "fp8_weights_direct": fp8_direct,
+        "heads_sharded": heads_sharded,
         "attainable": attain,
         "parity_sampled_rel_err": parity,
         "cpu_baseline": cpu,

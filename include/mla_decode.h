@@ -64,7 +64,7 @@ typedef enum {
   MLA_ERR_BAD_DIM = 2,             /* B, k_max, max_len or splits invalid */
   MLA_ERR_ALIGNMENT = 3,           /* base not 16-byte aligned / stride not 8 elements */
   MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < mla_workspace_bytes(B, num_splits)   */
-  MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths     */
+  MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths, or a head count other than 16/32/64/128 */
   MLA_ERR_HIP = 6,                 /* a HIP call failed: see mla_last_hip_error()     */
   MLA_ERR_RANGE = 7,               /* one sequence's cache or q_pe span exceeds 2 GiB */
   MLA_ERR_SCRATCH_LIMIT = 8        /* partials larger than the static scratch (noalloc) */
@@ -225,6 +225,41 @@ int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
 int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
                          const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh, float* lse,
                          uint32_t* status_dev, void* stream);
+
+/*
+ * Head-sharded step: the same calls for one GPU's share of the heads when
+ * the heads are split across GPUs ("Queries" page, init excerpt: wkv_b is a
+ * column-parallel layer and each rank holds n_local_heads heads; the decode
+ * excerpt on the "Query-key similarity" page views wkv_b per local head).
+ * n_heads is 16, 32, 64 or 128 (MLA_ERR_UNSUPPORTED otherwise) and every
+ * per-head array has n_heads heads: q_nope [B, n_heads, 128] and q_pe
+ * [B, n_heads, 64] (strides as in the 128-head calls), wkv_b
+ * [n_heads*256][512] (the rank's rows of the weight), q_abs and o_latent
+ * [B][n_heads][512], lse [B][n_heads], scores_out [B][n_heads][k_max], out
+ * [B, n_heads, 128], workspace >= mla_workspace_bytes_heads(n_heads, B, S).
+ * The selection and the latent cache are shared by all heads, so every rank
+ * reads every selected row; the decode launches the same workgroups as for
+ * 128 heads.  Otherwise each call is the 128-head call of the same name.
+ */
+size_t mla_workspace_bytes_heads(int32_t n_heads, int32_t B, int32_t num_splits);
+int mla_absorb_q_heads(int32_t n_heads, const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
+                       const void* wkv_b, void* q_abs, int32_t B, void* stream);
+int mla_sparse_decode_heads(int32_t n_heads, const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                            const void* kv, int64_t kv_sb, int64_t kv_st,
+                            const void* pe, int64_t pe_sb, int64_t pe_st,
+                            const int32_t* seq_lens, int32_t max_len,
+                            const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                            int32_t num_splits, void* workspace, size_t ws_bytes,
+                            void* o_latent, float* lse,
+                            uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                            float* scores_out, uint32_t* status_dev, void* stream);
+int mla_combine_heads(int32_t n_heads, const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                      void* o_latent, float* lse, uint32_t* status_dev, void* stream);
+int mla_value_up_heads(int32_t n_heads, const void* o_latent, const void* wkv_b, void* out, int64_t out_sb,
+                       int64_t out_sh, int32_t B, void* stream);
+int mla_combine_value_up_heads(int32_t n_heads, const void* workspace, size_t ws_bytes, int32_t B,
+                               int32_t num_splits, const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh,
+                               float* lse, uint32_t* status_dev, void* stream);
 
 /*
  * Sparse prefill ("Queries" page, prefill mode, mla-prefill excerpt): for

@@ -45,6 +45,16 @@ _status_string = _sig("mla_status_string", ctypes.c_char_p, [ctypes.c_int])
 _last_hip_error = _sig("mla_last_hip_error", ctypes.c_int, [])
 _plan = _sig("mla_plan", ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_i32)])
 _workspace_bytes = _sig("mla_workspace_bytes", _sz, [_i32, _i32])
+_workspace_bytes_h = _sig("mla_workspace_bytes_heads", _sz, [_i32, _i32, _i32])
+_absorb_h = _sig("mla_absorb_q_heads", ctypes.c_int, [_i32, _p, _i64, _i64, _p, _p, _i32, _p])
+_decode_h = _sig("mla_sparse_decode_heads", ctypes.c_int, [_i32] + [
+    _p, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i32, _p, _i32, _f32, _i32,
+    _i32, _p, _sz, _p, _p, _u32, _p, _i64, _p, _p, _p])
+_combine_h = _sig("mla_combine_heads", ctypes.c_int, [_i32, _p, _sz, _i32, _i32, _p, _p, _p, _p])
+_value_up_h = _sig("mla_value_up_heads", ctypes.c_int, [_i32, _p, _p, _p, _i64, _i64, _i32, _p])
+_combine_value_up_h = _sig("mla_combine_value_up_heads", ctypes.c_int,
+                           [_i32, _p, _sz, _i32, _i32, _p, _p, _i64, _i64, _p, _p, _p])
+HEAD_COUNTS = (16, 32, 64, 128)
 _absorb = _sig("mla_absorb_q", ctypes.c_int, [_p, _i64, _i64, _p, _p, _i32, _p])
 _decode = _sig("mla_sparse_decode", ctypes.c_int, [
     _p, _p, _i64, _i64,            # q_abs q_pe q_pe_sb q_pe_sh
@@ -141,25 +151,34 @@ def mla_plan(B: int, k_max: int, dense: bool, num_cus: Optional[int] = None):
     return s.value
 
 
-def mla_workspace_bytes(B: int, num_splits: int) -> int:
-    return int(_workspace_bytes(B, num_splits))
+def mla_workspace_bytes(B: int, num_splits: int, heads: int = HEADS) -> int:
+    return int(_workspace_bytes_h(heads, B, num_splits))
+
+
+def _heads(H: int) -> int:
+    if H not in HEAD_COUNTS:
+        raise ValueError(f"head count {H} not one of {HEAD_COUNTS}")
+    return H
 
 
 def mla_absorb_q(q_nope: torch.Tensor, wkv_b: torch.Tensor, q_abs: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
+    """q_nope [B, 1, H, 128] or [B, H, 128] with H = 128 or a head-sharded
+    share (16, 32, 64; wkv_b then holds those heads' H * 256 rows)."""
     _need(q_nope, "q_nope", torch.bfloat16)
     _need(wkv_b, "wkv_b", torch.bfloat16, 2)
     B, H, sb, sh = _bsh(q_nope)
-    if H != HEADS or q_nope.shape[-1] != NOPE or tuple(wkv_b.shape) != (HEADS * (NOPE + VALUE), LATENT):
+    _heads(H)
+    if q_nope.shape[-1] != NOPE or tuple(wkv_b.shape) != (H * (NOPE + VALUE), LATENT):
         raise ValueError("shape mismatch with the fixed model dimensions")
     if not wkv_b.is_contiguous():
         raise ValueError("wkv_b must be contiguous")
     if q_abs is None:
-        q_abs = torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=q_nope.device)
+        q_abs = torch.empty((B, H, LATENT), dtype=torch.bfloat16, device=q_nope.device)
     _need(q_abs, "q_abs", torch.bfloat16, 3)
-    if tuple(q_abs.shape) != (B, HEADS, LATENT) or not q_abs.is_contiguous():
-        raise ValueError("q_abs must be a contiguous [B,128,512] tensor")
-    _check("mla_absorb_q", _absorb(_ptr(q_nope), sb, sh, _ptr(wkv_b), _ptr(q_abs), B, _stream(stream)))
+    if tuple(q_abs.shape) != (B, H, LATENT) or not q_abs.is_contiguous():
+        raise ValueError("q_abs must be a contiguous [B,H,512] tensor")
+    _check("mla_absorb_q", _absorb_h(H, _ptr(q_nope), sb, sh, _ptr(wkv_b), _ptr(q_abs), B, _stream(stream)))
     return q_abs
 
 
@@ -173,9 +192,9 @@ def mla_sparse_decode(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indices, scal
     _need(kv, "kv", torch.bfloat16, 3)
     _need(pe, "pe", torch.bfloat16, 3)
     _need(seq_lens, "seq_lens", torch.int32, 1)
-    B = q_abs.shape[0]
+    B, H = q_abs.shape[0], _heads(q_abs.shape[1])
     Bq, Hq, qsb, qsh = _bsh(q_pe)
-    if Bq != B or Hq != HEADS or q_pe.shape[-1] != ROPE or kv.shape[-1] != LATENT or pe.shape[-1] != ROPE:
+    if Bq != B or Hq != H or q_pe.shape[-1] != ROPE or kv.shape[-1] != LATENT or pe.shape[-1] != ROPE:
         raise ValueError("shape mismatch with the fixed model dimensions")
     if kv.shape[0] < B or pe.shape[0] < B or seq_lens.shape[0] != B or kv.shape[1] < max_len or pe.shape[1] < max_len:
         raise ValueError("cache or seq_lens too small")
@@ -191,8 +210,8 @@ def mla_sparse_decode(q_abs, q_pe, kv, pe, seq_lens, max_len: int, indices, scal
         _need(bitmap, "bitmap", torch.int32, 2)
         words = bitmap.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("mla_sparse_decode", _decode(
-        _ptr(q_abs), _ptr(q_pe), qsb, qsh,
+    _check("mla_sparse_decode", _decode_h(
+        H, _ptr(q_abs), _ptr(q_pe), qsb, qsh,
         _ptr(kv), kv.stride(0), kv.stride(1),
         _ptr(pe), pe.stride(0), pe.stride(1),
         _ptr(seq_lens), int(max_len),
@@ -311,40 +330,46 @@ def mla_sparse_prefill(q_nope, q_pe, kv, pe, wkv_b, indices, scale: float, num_s
 
 
 def mla_combine(workspace, B: int, num_splits: int, o_latent, lse=None, status=None, stream=None):
+    """The heads come from o_latent [B, H, 512]."""
+    H = _heads(o_latent.shape[1])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("mla_combine", _combine(_ptr(workspace), ws_bytes, B, num_splits, _ptr(o_latent), _ptr(lse),
-                                   _ptr(status), _stream(stream)))
+    _check("mla_combine", _combine_h(H, _ptr(workspace), ws_bytes, B, num_splits, _ptr(o_latent), _ptr(lse),
+                                     _ptr(status), _stream(stream)))
 
 
 def mla_value_up(o_latent: torch.Tensor, wkv_b: torch.Tensor, out: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
     _need(o_latent, "o_latent", torch.bfloat16, 3)
     _need(wkv_b, "wkv_b", torch.bfloat16, 2)
-    B = o_latent.shape[0]
-    if not o_latent.is_contiguous() or tuple(o_latent.shape) != (B, HEADS, LATENT):
-        raise ValueError("o_latent must be a contiguous [B,128,512] tensor")
+    B, H = o_latent.shape[0], _heads(o_latent.shape[1])
+    if not o_latent.is_contiguous() or tuple(o_latent.shape) != (B, H, LATENT):
+        raise ValueError("o_latent must be a contiguous [B,H,512] tensor")
+    if tuple(wkv_b.shape) != (H * (NOPE + VALUE), LATENT):
+        raise ValueError("wkv_b must hold the H heads' rows")
     if out is None:
-        out = torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=o_latent.device)
+        out = torch.empty((B, 1, H, VALUE), dtype=torch.bfloat16, device=o_latent.device)
     _need(out, "out", torch.bfloat16)
     Bo, Ho, sb, sh = _bsh(out)
-    if Bo != B or Ho != HEADS or out.shape[-1] != VALUE:
-        raise ValueError("out must be [B,1,128,128] or [B,128,128]")
-    _check("mla_value_up", _value_up(_ptr(o_latent), _ptr(wkv_b), _ptr(out), sb, sh, B, _stream(stream)))
+    if Bo != B or Ho != H or out.shape[-1] != VALUE:
+        raise ValueError("out must be [B,1,H,128] or [B,H,128]")
+    _check("mla_value_up", _value_up_h(H, _ptr(o_latent), _ptr(wkv_b), _ptr(out), sb, sh, B, _stream(stream)))
     return out
 
 
 def mla_combine_value_up(workspace, B: int, num_splits: int, wkv_b: torch.Tensor,
                          out: Optional[torch.Tensor] = None, lse=None, status=None, stream=None) -> torch.Tensor:
+    """The heads come from wkv_b's rows (H * 256)."""
     _need(wkv_b, "wkv_b", torch.bfloat16, 2)
+    H = _heads(wkv_b.shape[0] // (NOPE + VALUE))
     if out is None:
-        out = torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=wkv_b.device)
+        out = torch.empty((B, 1, H, VALUE), dtype=torch.bfloat16, device=wkv_b.device)
     _need(out, "out", torch.bfloat16)
     Bo, Ho, sb, sh = _bsh(out)
-    if Bo != B or Ho != HEADS or out.shape[-1] != VALUE:
-        raise ValueError("out must be [B,1,128,128] or [B,128,128]")
+    if Bo != B or Ho != H or out.shape[-1] != VALUE:
+        raise ValueError("out must be [B,1,H,128] or [B,H,128]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("mla_combine_value_up", _combine_value_up(_ptr(workspace), ws_bytes, B, num_splits, _ptr(wkv_b),
-                                                     _ptr(out), sb, sh, _ptr(lse), _ptr(status), _stream(stream)))
+    _check("mla_combine_value_up", _combine_value_up_h(H, _ptr(workspace), ws_bytes, B, num_splits, _ptr(wkv_b),
+                                                       _ptr(out), sb, sh, _ptr(lse), _ptr(status), _stream(stream)))
     return out
 
 
@@ -457,16 +482,18 @@ class DecodeBuffers:
     workspace: Optional[torch.Tensor]
 
     @staticmethod
-    def allocate(B: int, k_max: int, dense: bool, device="cuda", num_splits=None):
+    def allocate(B: int, k_max: int, dense: bool, device="cuda", num_splits=None, heads: int = HEADS):
+        """Buffers for B sequences of `heads` heads (128, or a head-sharded
+        share: 16, 32, 64)."""
         if num_splits is None:
             num_splits = mla_plan(B, k_max, dense)
-        ws = mla_workspace_bytes(B, num_splits)
+        ws = mla_workspace_bytes(B, num_splits, _heads(heads))
         return DecodeBuffers(
             B=B, k_max=k_max, num_splits=num_splits,
-            q_abs=torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=device),
-            o_latent=torch.empty((B, HEADS, LATENT), dtype=torch.bfloat16, device=device),
-            lse=torch.empty((B, HEADS), dtype=torch.float32, device=device),
-            out=torch.empty((B, 1, HEADS, VALUE), dtype=torch.bfloat16, device=device),
+            q_abs=torch.empty((B, heads, LATENT), dtype=torch.bfloat16, device=device),
+            o_latent=torch.empty((B, heads, LATENT), dtype=torch.bfloat16, device=device),
+            lse=torch.empty((B, heads), dtype=torch.float32, device=device),
+            out=torch.empty((B, 1, heads, VALUE), dtype=torch.bfloat16, device=device),
             workspace=torch.empty(ws, dtype=torch.uint8, device=device) if ws else None,
         )
 
@@ -518,11 +545,12 @@ class StepLauncher:
                             (seq_lens, "seq_lens", torch.int32)):
             _need(t, name, dt)
         B = bufs.B
-        if (_bsh(q_nope)[:2] != (B, HEADS) or _bsh(q_pe)[:2] != (B, HEADS) or q_nope.shape[-1] != NOPE
+        Hq = _bsh(q_nope)[1]
+        if (_bsh(q_nope)[:2] != (B, Hq) or _bsh(q_pe)[:2] != (B, Hq) or q_nope.shape[-1] != NOPE
                 or q_pe.shape[-1] != ROPE or kv.dim() != 3 or pe.dim() != 3 or kv.shape[-1] != LATENT
                 or pe.shape[-1] != ROPE or kv.shape[0] < B or pe.shape[0] < B or seq_lens.shape != (B,)
                 or kv.shape[1] < max_len or pe.shape[1] < max_len
-                or tuple(wkv_b.shape) != (HEADS * (NOPE + VALUE), LATENT) or not wkv_b.is_contiguous()):
+                or (not fp8 and tuple(wkv_b.shape) != (Hq * (NOPE + VALUE), LATENT)) or not wkv_b.is_contiguous()):
             raise ValueError("shape mismatch with the fixed model dimensions or the buffers")
         if indices is not None:
             _need(indices, "indices", torch.int32, 2)
@@ -530,6 +558,9 @@ class StepLauncher:
                 raise ValueError("indices must be a contiguous int32 [B, k] tensor")
         st = _stream(stream)
         B = bufs.B
+        H = _heads(_bsh(q_nope)[1])
+        if fp8 and H != HEADS:
+            raise ValueError("the fp8 weight path takes all 128 heads")
         _, _, qn_sb, qn_sh = _bsh(q_nope)
         _, _, qp_sb, qp_sh = _bsh(q_pe)
         _, _, o_sb, o_sh = _bsh(bufs.out)
@@ -537,11 +568,11 @@ class StepLauncher:
         k_max = bufs.k_max if indices is None else indices.shape[1]
         absorb = ((_absorb_fp8, "mla_absorb_q_fp8", (_ptr(q_nope), qn_sb, qn_sh, _ptr(w_fp8), _ptr(w_scale),
                                                      _ptr(bufs.q_abs), B, None, st)) if fp8 else
-                  (_absorb, "mla_absorb_q", (_ptr(q_nope), qn_sb, qn_sh, _ptr(wkv_b), _ptr(bufs.q_abs), B, st)))
+                  (_absorb_h, "mla_absorb_q", (H, _ptr(q_nope), qn_sb, qn_sh, _ptr(wkv_b), _ptr(bufs.q_abs), B, st)))
         self._calls = [
             absorb,
-            (_decode, "mla_sparse_decode", (
-                _ptr(bufs.q_abs), _ptr(q_pe), qp_sb, qp_sh,
+            (_decode_h, "mla_sparse_decode", (
+                H, _ptr(bufs.q_abs), _ptr(q_pe), qp_sb, qp_sh,
                 _ptr(kv), kv.stride(0), kv.stride(1), _ptr(pe), pe.stride(0), pe.stride(1),
                 _ptr(seq_lens), int(max_len), _ptr(indices), int(k_max), float(scale), B,
                 bufs.num_splits, _ptr(bufs.workspace), ws_bytes, _ptr(bufs.o_latent), _ptr(bufs.lse),
@@ -552,19 +583,19 @@ class StepLauncher:
                 _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits, _ptr(w_fp8), _ptr(w_scale), _ptr(bufs.out), o_sb,
                 o_sh, _ptr(bufs.lse), None, st)))
         elif bufs.num_splits > 1:
-            self._calls.append((_combine_value_up, "mla_combine_value_up", (
-                _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits, _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh,
+            self._calls.append((_combine_value_up_h, "mla_combine_value_up", (
+                H, _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits, _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh,
                 _ptr(bufs.lse), None, st)))
         elif fp8:
             self._calls.append((_value_up_fp8, "mla_value_up_fp8", (
                 _ptr(bufs.o_latent), _ptr(w_fp8), _ptr(w_scale), _ptr(bufs.out), o_sb, o_sh, B, None, st)))
         else:
-            self._calls.append((_value_up, "mla_value_up", (
-                _ptr(bufs.o_latent), _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh, B, st)))
+            self._calls.append((_value_up_h, "mla_value_up", (
+                H, _ptr(bufs.o_latent), _ptr(wkv_b), _ptr(bufs.out), o_sb, o_sh, B, st)))
         # The separate merge of the split partials (for timing the attention
         # part alone): mla_combine into bufs.o_latent and bufs.lse.
-        self._combine = (_combine, "mla_combine", (_ptr(bufs.workspace), ws_bytes, B, bufs.num_splits,
-                                                   _ptr(bufs.o_latent), _ptr(bufs.lse), None, st))
+        self._combine = (_combine_h, "mla_combine", (H, _ptr(bufs.workspace), ws_bytes, B, bufs.num_splits,
+                                                     _ptr(bufs.o_latent), _ptr(bufs.lse), None, st))
 
     @staticmethod
     def _run(call):

@@ -28,6 +28,10 @@ int hip_status(int err) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Head counts a call may take: all 128 heads, or one GPU's share of them
+// when the heads are sharded across GPUs.
+bool heads_ok(int32_t H) { return H == 16 || H == 32 || H == 64 || H == 128; }
+
 // Index slots per split: ceil(k_max / S) rounded up to whole key blocks.
 int64_t split_chunk(int32_t k_max, int32_t S) { return ceil_div(ceil_div(k_max, S), 32) * 32; }
 
@@ -44,7 +48,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_BAD_DIM: return "invalid size, split count or head-group count";
     case MLA_ERR_ALIGNMENT: return "pointer not 16-byte aligned or stride not a multiple of 8 elements";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_workspace_bytes()";
-    case MLA_ERR_UNSUPPORTED: return "stride smaller than the fixed row width";
+    case MLA_ERR_UNSUPPORTED: return "stride smaller than the fixed row width, or a head count other than 16/32/64/128";
     case MLA_ERR_HIP: return "HIP runtime error (see mla_last_hip_error)";
     case MLA_ERR_RANGE: return "a sequence's cache or q_pe span exceeds 2 GiB";
     case MLA_ERR_SCRATCH_LIMIT: return "the split partials exceed the library's static scratch (mla_noalloc_scratch_bytes)";
@@ -54,12 +58,14 @@ const char* mla_status_string(int status) {
 
 int mla_last_hip_error(void) { return g_last_hip_error; }
 
-size_t mla_workspace_bytes(int32_t B, int32_t num_splits) {
-  if (B < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
+size_t mla_workspace_bytes_heads(int32_t n_heads, int32_t B, int32_t num_splits) {
+  if (!heads_ok(n_heads) || B < 1 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return 0;
   if (num_splits == 1) return 0;
-  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  const size_t units = (size_t)num_splits * (size_t)B * n_heads;
   return units * MLA_LATENT_DIM * sizeof(uint16_t) + units * 2 * sizeof(float);
 }
+
+size_t mla_workspace_bytes(int32_t B, int32_t num_splits) { return mla_workspace_bytes_heads(MLA_HEADS, B, num_splits); }
 
 // Cost model (in nanoseconds) over splits 1..64, one workgroup per CU:
 //  * fixed: every round of workgroups loads its query tile and writes its
@@ -96,7 +102,8 @@ int mla_plan(int32_t B, int32_t k_max, int32_t dense, int32_t num_cus, int32_t* 
 namespace {
 
 int absorb_impl(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh, const void* wkv_b,
-                const mla::Fp8Weight& fp8, void* q_abs, int32_t B, void* stream) {
+                const mla::Fp8Weight& fp8, void* q_abs, int32_t B, void* stream, int32_t H = MLA_HEADS) {
+  if (!heads_ok(H)) return MLA_ERR_UNSUPPORTED;
   if (!q_nope || !q_abs || (!wkv_b && !fp8.w_fp8)) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536) return MLA_ERR_BAD_DIM;
   if (!aligned16(q_nope) || !aligned16(q_abs) || !stride8(q_nope_sb) || !stride8(q_nope_sh) ||
@@ -112,6 +119,7 @@ int absorb_impl(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh, const 
   a.wkv_b = static_cast<const uint16_t*>(wkv_b);
   a.q_abs = static_cast<uint16_t*>(q_abs);
   a.B = B;
+  a.H = H;
   a.fp8 = fp8;
   return hip_status(mla::launch_absorb(a, stream));
 }
@@ -138,6 +146,12 @@ int mla_absorb_q(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
   return absorb_impl(q_nope, q_nope_sb, q_nope_sh, wkv_b, mla::Fp8Weight{}, q_abs, B, stream);
 }
 
+int mla_absorb_q_heads(int32_t n_heads, const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh,
+                       const void* wkv_b, void* q_abs, int32_t B, void* stream) {
+  if (!wkv_b) return MLA_ERR_NULL_POINTER;
+  return absorb_impl(q_nope, q_nope_sb, q_nope_sh, wkv_b, mla::Fp8Weight{}, q_abs, B, stream, n_heads);
+}
+
 int mla_absorb_q_fp8(const void* q_nope, int64_t q_nope_sb, int64_t q_nope_sh, const void* w_fp8,
                      const float* w_scale, void* q_abs, int32_t B, void* w_formed, void* stream) {
   mla::Fp8Weight f;
@@ -161,7 +175,8 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
                    void* o_latent, float* lse,
                    uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
                    float* scores_out, uint32_t* status_dev, mla::DecodeArgs* out,
-                   int32_t prefill_T = 0) {
+                   int32_t prefill_T = 0, int32_t H = MLA_HEADS) {
+  if (!heads_ok(H)) return MLA_ERR_UNSUPPORTED;
   // prefill_T > 0: prefill rows (B = prompts * prefill_T, token r % T of
   // prompt r / T, causal lengths, no seq_lens, max_len = T).
   if (!q_abs || !q_pe || !kv || !pe || (!seq_lens && prefill_T == 0)) return MLA_ERR_NULL_POINTER;
@@ -178,7 +193,7 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
   if (kv_st < MLA_LATENT_DIM || pe_st < MLA_ROPE_DIM) return MLA_ERR_UNSUPPORTED;
   const int64_t span_limit = ((int64_t)1 << 31) - 1;
   if ((int64_t)max_len * kv_st * 2 > span_limit || (int64_t)max_len * pe_st * 2 > span_limit ||
-      ((int64_t)(MLA_HEADS - 1) * q_pe_sh + MLA_ROPE_DIM) * 2 > span_limit)
+      ((int64_t)(H - 1) * q_pe_sh + MLA_ROPE_DIM) * 2 > span_limit)
     return MLA_ERR_RANGE;
   if (num_splits == 1) {
     if (!o_latent) return MLA_ERR_NULL_POINTER;
@@ -186,7 +201,7 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
   } else {
     if (!workspace) return MLA_ERR_NULL_POINTER;
     if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
-    if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < mla_workspace_bytes_heads(H, B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
   if (flags & MLA_FLAG_VALIDATE) {
     if (!status_dev || !attended_bitmap) return MLA_ERR_NULL_POINTER;
@@ -211,12 +226,13 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
   a.k_max = k_max;
   a.chunk = (int32_t)chunk;
   a.B = B;
+  a.H = H;
   a.S = num_splits;
   a.causal = prefill_T > 0 ? 1 : 0;
   a.rows_per_seq = prefill_T > 0 ? prefill_T : 1;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  const size_t units = (size_t)num_splits * (size_t)B * H;
   a.part_o = num_splits > 1 ? static_cast<uint16_t*>(workspace) : nullptr;
   a.part_ml = num_splits > 1
                   ? reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) + units * MLA_LATENT_DIM)
@@ -235,6 +251,23 @@ int prepare_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t
 
 extern "C" {
 
+int mla_sparse_decode_heads(int32_t n_heads, const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
+                            const void* kv, int64_t kv_sb, int64_t kv_st,
+                            const void* pe, int64_t pe_sb, int64_t pe_st,
+                            const int32_t* seq_lens, int32_t max_len,
+                            const int32_t* indices, int32_t k_max, float scale, int32_t B,
+                            int32_t num_splits, void* workspace, size_t ws_bytes,
+                            void* o_latent, float* lse,
+                            uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
+                            float* scores_out, uint32_t* status_dev, void* stream) {
+  mla::DecodeArgs a;
+  const int st = prepare_decode(q_abs, q_pe, q_pe_sb, q_pe_sh, kv, kv_sb, kv_st, pe, pe_sb, pe_st, seq_lens,
+                                max_len, indices, k_max, scale, B, num_splits, workspace, ws_bytes, o_latent, lse,
+                                flags, attended_bitmap, bitmap_words, scores_out, status_dev, &a, 0, n_heads);
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_decode(a, stream));
+}
+
 int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int64_t q_pe_sh,
                       const void* kv, int64_t kv_sb, int64_t kv_st,
                       const void* pe, int64_t pe_sb, int64_t pe_st,
@@ -244,12 +277,9 @@ int mla_sparse_decode(const void* q_abs, const void* q_pe, int64_t q_pe_sb, int6
                       void* o_latent, float* lse,
                       uint32_t flags, uint32_t* attended_bitmap, int64_t bitmap_words,
                       float* scores_out, uint32_t* status_dev, void* stream) {
-  mla::DecodeArgs a;
-  const int st = prepare_decode(q_abs, q_pe, q_pe_sb, q_pe_sh, kv, kv_sb, kv_st, pe, pe_sb, pe_st, seq_lens,
-                                max_len, indices, k_max, scale, B, num_splits, workspace, ws_bytes, o_latent, lse,
-                                flags, attended_bitmap, bitmap_words, scores_out, status_dev, &a);
-  if (st != MLA_OK) return st;
-  return hip_status(mla::launch_decode(a, stream));
+  return mla_sparse_decode_heads(MLA_HEADS, q_abs, q_pe, q_pe_sb, q_pe_sh, kv, kv_sb, kv_st, pe, pe_sb, pe_st,
+                                 seq_lens, max_len, indices, k_max, scale, B, num_splits, workspace, ws_bytes,
+                                 o_latent, lse, flags, attended_bitmap, bitmap_words, scores_out, status_dev, stream);
 }
 
 size_t mla_noalloc_scratch_bytes(void) { return mla::kScratchBytes; }
@@ -291,6 +321,7 @@ int mla_sparse_decode_noalloc(const void* q_abs, const void* q_pe, int64_t q_pe_
   c.part_ml = a.part_ml;
   c.B = B;
   c.S = num_splits;
+  c.H = MLA_HEADS;
   c.o_latent = static_cast<uint16_t*>(o_latent);
   c.lse = lse;
   c.status = (flags & MLA_FLAG_VALIDATE) ? status_dev : nullptr;
@@ -343,6 +374,7 @@ int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
   ab.wkv_b = static_cast<const uint16_t*>(wkv_b);
   ab.q_abs = static_cast<uint16_t*>(q_abs);
   ab.B = rows;
+  ab.H = MLA_HEADS;
   st = hip_status(mla::launch_absorb(ab, stream));
   if (st != MLA_OK) return st;
   st = hip_status(mla::launch_decode(d, stream));
@@ -353,6 +385,7 @@ int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
   v.out_sb = out_st;
   v.out_sh = out_sh;
   v.B = rows;
+  v.H = MLA_HEADS;
   if (num_splits == 1) {
     v.o_latent = static_cast<const uint16_t*>(rest);
   } else {
@@ -366,23 +399,30 @@ int mla_sparse_prefill(const void* q_nope, int64_t q_nope_st, int64_t q_nope_sh,
   return hip_status(mla::launch_value_up(v, stream));
 }
 
-int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
-                void* o_latent, float* lse, uint32_t* status_dev, void* stream) {
+int mla_combine_heads(int32_t n_heads, const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                      void* o_latent, float* lse, uint32_t* status_dev, void* stream) {
+  if (!heads_ok(n_heads)) return MLA_ERR_UNSUPPORTED;
   if (B < 1 || B > 65536 || num_splits < 1 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
   if (num_splits == 1) return MLA_OK;
   if (!workspace || !o_latent) return MLA_ERR_NULL_POINTER;
   if (!aligned16(workspace) || !aligned16(o_latent)) return MLA_ERR_ALIGNMENT;
-  if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  if (ws_bytes < mla_workspace_bytes_heads(n_heads, B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t units = (size_t)num_splits * (size_t)B * n_heads;
   mla::CombineArgs a;
   a.part_o = static_cast<const uint16_t*>(workspace);
   a.part_ml = reinterpret_cast<const float*>(static_cast<const uint16_t*>(workspace) + units * MLA_LATENT_DIM);
   a.B = B;
   a.S = num_splits;
+  a.H = n_heads;
   a.o_latent = static_cast<uint16_t*>(o_latent);
   a.lse = lse;
   a.status = status_dev;
   return hip_status(mla::launch_combine(a, stream));
+}
+
+int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
+                void* o_latent, float* lse, uint32_t* status_dev, void* stream) {
+  return mla_combine_heads(MLA_HEADS, workspace, ws_bytes, B, num_splits, o_latent, lse, status_dev, stream);
 }
 
 }  // extern "C"
@@ -390,7 +430,8 @@ int mla_combine(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_s
 namespace {
 
 int value_up_impl(const void* o_latent, const void* wkv_b, const mla::Fp8Weight& fp8, void* out,
-                  int64_t out_sb, int64_t out_sh, int32_t B, void* stream) {
+                  int64_t out_sb, int64_t out_sh, int32_t B, void* stream, int32_t H = MLA_HEADS) {
+  if (!heads_ok(H)) return MLA_ERR_UNSUPPORTED;
   if (!o_latent || !out || (!wkv_b && !fp8.w_fp8)) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536) return MLA_ERR_BAD_DIM;
   if (!aligned16(o_latent) || (wkv_b && !aligned16(wkv_b)) || !aligned16(out) || !stride8(out_sb) ||
@@ -403,20 +444,22 @@ int value_up_impl(const void* o_latent, const void* wkv_b, const mla::Fp8Weight&
   a.out_sb = out_sb;
   a.out_sh = out_sh;
   a.B = B;
+  a.H = H;
   a.fp8 = fp8;
   return hip_status(mla::launch_value_up(a, stream));
 }
 
 int combine_value_up_impl(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,
                           const void* wkv_b, const mla::Fp8Weight& fp8, void* out, int64_t out_sb, int64_t out_sh,
-                          float* lse, uint32_t* status_dev, void* stream) {
+                          float* lse, uint32_t* status_dev, void* stream, int32_t H = MLA_HEADS) {
+  if (!heads_ok(H)) return MLA_ERR_UNSUPPORTED;
   if (B < 1 || B > 65536 || num_splits < 2 || num_splits > MLA_MAX_SPLITS) return MLA_ERR_BAD_DIM;
   if (!workspace || !out || (!wkv_b && !fp8.w_fp8)) return MLA_ERR_NULL_POINTER;
   if (!aligned16(workspace) || (wkv_b && !aligned16(wkv_b)) || !aligned16(out) || !stride8(out_sb) ||
       !stride8(out_sh))
     return MLA_ERR_ALIGNMENT;
-  if (ws_bytes < mla_workspace_bytes(B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  const size_t units = (size_t)num_splits * (size_t)B * MLA_HEADS;
+  if (ws_bytes < mla_workspace_bytes_heads(H, B, num_splits)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  const size_t units = (size_t)num_splits * (size_t)B * H;
   if (units * 8 > (size_t)INT32_MAX) return MLA_ERR_RANGE;  // (max, sum) addressed with 32-bit offsets
   mla::ValueUpArgs a = {};
   a.o_latent = nullptr;
@@ -428,6 +471,7 @@ int combine_value_up_impl(const void* workspace, size_t ws_bytes, int32_t B, int
   a.part_o = static_cast<const uint16_t*>(workspace);
   a.part_ml = reinterpret_cast<const float*>(static_cast<const uint16_t*>(workspace) + units * MLA_LATENT_DIM);
   a.S = num_splits;
+  a.H = H;
   a.lse = lse;
   a.status = status_dev;
   a.fp8 = fp8;
@@ -442,6 +486,12 @@ int mla_value_up(const void* o_latent, const void* wkv_b, void* out,
                  int64_t out_sb, int64_t out_sh, int32_t B, void* stream) {
   if (!wkv_b) return MLA_ERR_NULL_POINTER;
   return value_up_impl(o_latent, wkv_b, mla::Fp8Weight{}, out, out_sb, out_sh, B, stream);
+}
+
+int mla_value_up_heads(int32_t n_heads, const void* o_latent, const void* wkv_b, void* out, int64_t out_sb,
+                       int64_t out_sh, int32_t B, void* stream) {
+  if (!wkv_b) return MLA_ERR_NULL_POINTER;
+  return value_up_impl(o_latent, wkv_b, mla::Fp8Weight{}, out, out_sb, out_sh, B, stream, n_heads);
 }
 
 int mla_value_up_fp8(const void* o_latent, const void* w_fp8, const float* w_scale, void* out,
@@ -478,6 +528,14 @@ int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int3
   if (!wkv_b) return MLA_ERR_NULL_POINTER;
   return combine_value_up_impl(workspace, ws_bytes, B, num_splits, wkv_b, mla::Fp8Weight{}, out, out_sb, out_sh,
                                lse, status_dev, stream);
+}
+
+int mla_combine_value_up_heads(int32_t n_heads, const void* workspace, size_t ws_bytes, int32_t B,
+                               int32_t num_splits, const void* wkv_b, void* out, int64_t out_sb, int64_t out_sh,
+                               float* lse, uint32_t* status_dev, void* stream) {
+  if (!wkv_b) return MLA_ERR_NULL_POINTER;
+  return combine_value_up_impl(workspace, ws_bytes, B, num_splits, wkv_b, mla::Fp8Weight{}, out, out_sb, out_sh,
+                               lse, status_dev, stream, n_heads);
 }
 
 int mla_combine_value_up_fp8(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,

@@ -29,6 +29,7 @@ struct AbsorbArgs {
   const uint16_t* wkv_b;
   uint16_t* q_abs;
   int32_t B;
+  int32_t H;                // heads (128, or a head-sharded share: 16, 32, 64)
   Fp8Weight fp8;
 };
 
@@ -46,6 +47,7 @@ struct DecodeArgs {
   int32_t k_max;
   int32_t chunk;            // index slots per split (multiple of 32)
   int32_t B;                // query rows (sequences in decode, B * T tokens in prefill)
+  int32_t H;                // heads (128, or a head-sharded share: 16, 32, 64)
   int32_t S;                // splits
   int32_t causal;           // 0: decode (row b = sequence b, length seq_lens[b]);
                             // 1: prefill, row r = token r % T of prompt r / T
@@ -68,6 +70,7 @@ struct CombineArgs {
   const uint16_t* part_o;
   const float* part_ml;
   int32_t B, S;
+  int32_t H;
   uint16_t* o_latent;
   float* lse;
   uint32_t* status;
@@ -79,6 +82,7 @@ struct ValueUpArgs {
   uint16_t* out;
   int64_t out_sb, out_sh;
   int32_t B;
+  int32_t H;
   // Fused combine (o_latent == NULL): partials of mla_sparse_decode.
   const uint16_t* part_o;
   const float* part_ml;

@@ -250,8 +250,8 @@ constexpr int kAbsLds = 2 * kAbsQ + 4 * kAbsQTile;
 template <bool FP8>
 __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
   __shared__ __attribute__((aligned(1024))) char wt[kAbsLds];
-  const int h = blockIdx.x & (kHeads - 1);
-  const int ch = blockIdx.x >> 7;
+  const int h = (int)blockIdx.x % a.H;
+  const int ch = (int)blockIdx.x / a.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, i16 = lane & 15, gm = (lane >> 4) & 1;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
       const int bb = bt * 32 + r;
       const uint4 val = *reinterpret_cast<const uint4*>(ot + r * 256 + ((c ^ (r & 15)) << 4));
       if (bb < a.B)
-        *reinterpret_cast<uint4*>(a.q_abs + ((int64_t)bb * kHeads + h) * kLatent + ch * 256 + 128 * Q + 8 * c) = val;
+        *reinterpret_cast<uint4*>(a.q_abs + ((int64_t)bb * a.H + h) * kLatent + ch * 256 + 128 * Q + 8 * c) = val;
     }
   };
 
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   __shared__ float2 mltab[FUSED ? 4 * kMlWave : 1];
   static_assert(32 % (SPP * RPW) == 0, "W_UV loads spread evenly over the first merge pass");
   const int ntiles = (a.B + ROWS - 1) / ROWS;
-  const int units = kHeads * ntiles;
+  const int units = a.H * ntiles;
   const int per_xcd = (units + 7) >> 3;
   const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (unit >= units) return;
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   const int r0 = RPW * wave;              // first tile row of this wave
 
   const int S = FUSED ? a.S : 1;
-  const int64_t sstride = (int64_t)a.B * kHeads;  // rows per split
+  const int64_t sstride = (int64_t)a.B * a.H;  // rows per split
   // fp8: the four scale blocks of W_UV,h (row block 2h + 1) and whether each
   // needs the exact rounding rule, settled before anything else is in flight.
   float wsc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -521,14 +521,14 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   auto gather = [&](int c0) {
     if (n == 0) return;
     const int ps = pass_splits(c0);
-    const int64_t row0 = (int64_t)(b0 + r0) * kHeads + h;
+    const int64_t row0 = (int64_t)(b0 + r0) * a.H + h;
     for (int c = 0; c < ps; ++c) {
       const uint16_t* base = FUSED ? a.part_o + ((int64_t)(c0 + c) * sstride + row0) * kLatent
                                    : a.o_latent + row0 * kLatent;
-      const i32x4 rs = buffer_rsrc(base, (uint32_t)(n - 1) * kHeads * kLatent * 2u + 1024u);
+      const i32x4 rs = buffer_rsrc(base, (uint32_t)(n - 1) * (uint32_t)a.H * kLatent * 2u + 1024u);
       for (int j = 0; j < n; ++j)
         dma16(rs, lds0 + (uint32_t)(slot_of(c * n + j) * kOtRow),
-              (uint32_t)j * kHeads * kLatent * 2u + 16u * (uint32_t)lane);
+              (uint32_t)j * (uint32_t)a.H * kLatent * 2u + 16u * (uint32_t)lane);
     }
   };
   // Wait until at most k vector-memory operations are outstanding, k rounded
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
   const int nml = (RPW * 2 * G + 63) >> 6;  // table DMAs: 64 entries each
   float2* mlt = mltab + (FUSED ? wave * kMlWave : 0);
   if constexpr (FUSED) {
-    const int64_t bh0 = (int64_t)min(b0 + r0, a.B - 1) * kHeads + h;
+    const int64_t bh0 = (int64_t)min(b0 + r0, a.B - 1) * a.H + h;
     const float* mlb = a.part_ml + bh0 * 2;
     const uint32_t rng = (uint32_t)(((int64_t)S * sstride - bh0) * 8);
     const i32x4 rml = buffer_rsrc(mlb, rng);
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
     for (int i = 0; i < nml; ++i) {
       const int e = 64 * i + lane;  // entry index: (j G + sp) 2 + f
       const int j = e >> (gsh + 1), sp = (e >> 1) & (G - 1), f = e & 1;
-      const uint32_t off = (sp < S && j < RPW) ? (uint32_t)(sp * sstride * 8 + j * kHeads * 8 + 4 * f) : 0xfffffff0u;
+      const uint32_t off = (sp < S && j < RPW) ? (uint32_t)(sp * sstride * 8 + j * a.H * 8 + 4 * f) : 0xfffffff0u;
       dma4(rml, mdst + 256u * (uint32_t)i, off);
     }
   }
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
       for (int o = 1; o < G; o <<= 1) L += __shfl_xor(L, o);
       if (j < RPW && sp < S) wt[j * 64 + sp] = L > 0.f ? e / L : __builtin_nanf("");
       if (j < RPW && sp == 0 && r0 + j < nrows) {
-        const int64_t bh = (int64_t)(b0 + r0 + j) * kHeads + h;
+        const int64_t bh = (int64_t)(b0 + r0 + j) * a.H + h;
         if (a.lse != nullptr) a.lse[bh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
         if (a.status != nullptr && h == 0 && !(L > 0.f)) atomicOr(a.status, 4u);
       }
@@ -840,9 +840,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
                   : (uint32_t)(kOffQ + kQWave * wave + m * kBlk * 128);
   };
   auto stage_query = [&](int m0, int m1) __attribute__((always_inline)) {
-    const i32x4 rq = buffer_rsrc(a.q_abs + (int64_t)b * kHeads * kLatent, (uint32_t)(kHeads * kLatent * 2));
+    // Heads past a.H (a head-sharded call) lie past both ranges and load zeros.
+    const i32x4 rq = buffer_rsrc(a.q_abs + (int64_t)b * a.H * kLatent, (uint32_t)(a.H * kLatent * 2));
     const i32x4 rp = buffer_rsrc(a.q_pe + (int64_t)b * a.q_pe_sb,
-                                 (uint32_t)(((int64_t)(kHeads - 1) * a.q_pe_sh + kRope) * 2));
+                                 (uint32_t)(((int64_t)(a.H - 1) * a.q_pe_sh + kRope) * 2));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t r = (uint32_t)(8 * g + (lane >> 3));
@@ -928,8 +929,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   for (int st = 28; st < 36; ++st) asm volatile("" : "+v"(qf[st]));
   __syncthreads();
 
-  uint16_t* dst = !SPLIT ? a.o_latent + (int64_t)b * kHeads * kLatent
-                             : a.part_o + ((int64_t)s * a.B + b) * kHeads * kLatent;
+  uint16_t* dst = !SPLIT ? a.o_latent + (int64_t)b * a.H * kLatent
+                             : a.part_o + ((int64_t)s * a.B + b) * a.H * kLatent;
   if (nblk == 0) {
     // The query rows may still be landing in this workgroup's LDS.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -938,14 +939,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
     // merge gives it no weight.  (max, sum) = (-inf, 0).  Everything below
     // may then assume a block.
     const uint32_t fb = !SPLIT ? 0x7fc07fc0u : 0u;
-    for (int i = tid; i < kHeads * kLatent / 8; i += 256)
+    for (int i = tid; i < a.H * kLatent / 8; i += 256)
       reinterpret_cast<uint4*>(dst)[i] = uint4{fb, fb, fb, fb};
-    if (tid < kHeads) {
+    if (tid < a.H) {
       if constexpr (!SPLIT) {
-        if (a.lse != nullptr) a.lse[(int64_t)b * kHeads + tid] = -INFINITY;
+        if (a.lse != nullptr) a.lse[(int64_t)b * a.H + tid] = -INFINITY;
         if (validate && tid == 0) atomicOr(a.status, 4u);
       } else {
-        float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + tid) * 2;
+        float* pml = a.part_ml + (((int64_t)s * a.B + b) * a.H + tid) * 2;
         pml[0] = -INFINITY;
         pml[1] = 0.f;
       }
@@ -1043,7 +1044,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   };
   // Raw scores of block j (scale applied, -inf where masked).
   auto write_scores = [&](int j, const f32x16& x, uint32_t vmj) __attribute__((always_inline)) {
-    float* so = a.scores + ((int64_t)b * kHeads + head) * a.k_max + s0 + j * kBlk;
+    if (head >= a.H) return;
+    float* so = a.scores + ((int64_t)b * a.H + head) * a.k_max + s0 + j * kBlk;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int kloc = 8 * (v >> 2) + 4 * hh + (v & 3);
@@ -1259,13 +1261,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (hh == 0) {
+    if (hh == 0 && head < a.H) {
       if constexpr (!SPLIT) {
         if (a.lse != nullptr)
-          a.lse[(int64_t)b * kHeads + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+          a.lse[(int64_t)b * a.H + head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
         if (validate && !(l_run > 0.f)) atomicOr(a.status, 4u);
       } else {
-        float* pml = a.part_ml + (((int64_t)s * a.B + b) * kHeads + head) * 2;
+        float* pml = a.part_ml + (((int64_t)s * a.B + b) * a.H + head) * 2;
         pml[0] = m_run;
         pml[1] = l_run;
       }
@@ -1276,6 +1278,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 #pragma unroll 8
   for (int r = 0; r < 32; ++r) {
     const int h = 32 * wave + r;
+    if (h >= a.H) break;  // heads past a head-sharded call's share: not stored
     uint4 v = *reinterpret_cast<const uint4*>(smem + h * kTilePitch + 16 * lane);
     if (r & 16) v = uint4{v.z, v.w, v.x, v.y};
     *reinterpret_cast<uint4*>(dst + (int64_t)h * kLatent + 8 * lane) = v;
@@ -1290,11 +1293,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
-  const int b = blockIdx.x >> 6;
-  const int head = (blockIdx.x & 63) * 2 + (threadIdx.x >> 7);
+  const int hp = a.H / 2;  // head pairs per sequence
+  const int b = (int)blockIdx.x / hp;
+  const int head = ((int)blockIdx.x % hp) * 2 + (threadIdx.x >> 7);
   const int col = (threadIdx.x & 127) * 4;
-  const int64_t stride_s = (int64_t)a.B * kHeads;
-  const int64_t bh = (int64_t)b * kHeads + head;
+  const int64_t stride_s = (int64_t)a.B * a.H;
+  const int64_t bh = (int64_t)b * a.H + head;
   // Splits in groups of G whose loads are all in flight together (one at a
   // time, a 32-split merge is 32 memory latencies long); a group's slots past
   // S re-read split S - 1 (in bounds) and get weight 0.  The sums run over
@@ -1444,9 +1448,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 
 int launch_absorb(const AbsorbArgs& a, void* stream) {
   if (a.fp8.w_fp8 != nullptr)
-    hipLaunchKernelGGL(absorb_kernel<true>, dim3(kHeads * 2), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(absorb_kernel<true>, dim3(a.H * 2), dim3(256), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL(absorb_kernel<false>, dim3(kHeads * 2), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(absorb_kernel<false>, dim3(a.H * 2), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
@@ -1468,9 +1472,10 @@ int launch_output_proj(const OutProjArgs& a, void* stream) {
 }
 
 int launch_combine(const CombineArgs& a, void* stream) {
-  if (a.S <= 2) hipLaunchKernelGGL(combine_kernel<2>, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
-  else if (a.S <= 4) hipLaunchKernelGGL(combine_kernel<4>, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
-  else hipLaunchKernelGGL(combine_kernel<8>, dim3(a.B * 64), dim3(256), 0, (hipStream_t)stream, a);
+  const dim3 grid(a.B * (a.H / 2));
+  if (a.S <= 2) hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, (hipStream_t)stream, a);
+  else if (a.S <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, (hipStream_t)stream, a);
+  else hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
@@ -1497,7 +1502,7 @@ int launch_value_up(const ValueUpArgs& a, void* stream) {
   const bool small = a.B <= 32;
   const int rows = small ? 16 : 32;
   const bool two = a.o_latent != nullptr || a.S <= 2;
-  const int units = kHeads * ((a.B + rows - 1) / rows);
+  const int units = a.H * ((a.B + rows - 1) / rows);
   const dim3 grid(8 * ((units + 7) / 8));
   const hipStream_t st = (hipStream_t)stream;
   if (a.fp8.w_fp8 != nullptr) launch_value_up_t<true>(a, grid, small, two, st);

@@ -218,3 +218,24 @@ def test_noalloc_host_checks(lib):
     assert lib.mla_sparse_decode_noalloc(*args) == NULLP
     args[17] = a + 8
     assert lib.mla_sparse_decode_noalloc(*args) == ALIGN
+
+
+def test_heads_host_checks(lib):
+    """The head-sharded calls take 16, 32, 64 or 128 heads and reject others
+    on the host (MLA_ERR_UNSUPPORTED); workspace sizes scale with the heads."""
+    a = FAKE
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mla_workspace_bytes_heads.restype = sz
+    lib.mla_workspace_bytes_heads.argtypes = [i32, i32, i32]
+    lib.mla_absorb_q_heads.argtypes = [i32, p, i64, i64, p, p, i32, p]
+    lib.mla_value_up_heads.argtypes = [i32, p, p, p, i64, i64, i32, p]
+    lib.mla_combine_heads.argtypes = [i32, p, sz, i32, i32, p, p, p, p]
+    for H in (16, 32, 64, 128):
+        assert lib.mla_workspace_bytes_heads(H, 64, 4) == 4 * 64 * H * (512 * 2 + 2 * 4)
+    assert lib.mla_workspace_bytes_heads(128, 64, 4) == lib.mla_workspace_bytes(64, 4)
+    assert lib.mla_workspace_bytes_heads(48, 64, 4) == 0
+    for H in (0, 8, 48, 96, 256):
+        assert lib.mla_absorb_q_heads(H, a, 8192, 128, a, a, 4, None) == UNSUP
+        assert lib.mla_value_up_heads(H, a, a, a, 8192, 128, 4, None) == UNSUP
+        assert lib.mla_combine_heads(H, a, 1 << 30, 4, 2, a, None, None, None) == UNSUP
+    assert lib.mla_absorb_q_heads(64, None, 8192, 128, a, a, 4, None) == NULLP
