@@ -352,7 +352,9 @@ int mla_combine_value_up_fp8(const void* workspace, size_t ws_bytes, int32_t B, 
  *        are written; 2-byte aligned.
  * fp32 accumulation, one rounding to bf16.  Launches one kernel per 64 rows
  * of the batch.  Errors: MLA_ERR_NULL_POINTER, MLA_ERR_BAD_DIM (B outside
- * 1 .. 65536, a row stride below the row width), MLA_ERR_ALIGNMENT, MLA_ERR_HIP.
+ * 1 .. 65536, a row stride below the row width), MLA_ERR_ALIGNMENT,
+ * MLA_ERR_RANGE ((63 * x_sb + 16384) * 2 bytes must stay below 4 GiB),
+ * MLA_ERR_HIP.
  */
 int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
                     void* stream);

@@ -508,6 +508,8 @@ int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int6
   if (B < 1 || B > 65536 || x_sb < mla::kWoIn || out_sb < mla::kWoOut) return MLA_ERR_BAD_DIM;
   if (!aligned16(x) || !aligned16(wo) || !stride8(x_sb) || (reinterpret_cast<uintptr_t>(out) & 1u) != 0)
     return MLA_ERR_ALIGNMENT;
+  // The rows of one launch (up to 64) are read with 32-bit byte offsets.
+  if ((63 * x_sb + mla::kWoIn) * 2 > (int64_t)UINT32_MAX) return MLA_ERR_RANGE;
   for (int32_t b0 = 0; b0 < B; b0 += 64) {
     mla::OutProjArgs a;
     a.x = static_cast<const uint16_t*>(x) + (int64_t)b0 * x_sb;

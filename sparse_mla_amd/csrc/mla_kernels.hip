@@ -1349,71 +1349,106 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
 // output projection ("Attention update" page, mla-output): each sequence's
 // head outputs flattened (i = 128 h + d) and projected to the model width,
 //   out[b][o] = sum_i x[b][i] wo[o][i],  wo [7168][16384] (a linear weight).
-// HBM-bound on wo (235 MB): each weight is read once per launch of up to 64
-// batch rows.  Workgroup = 32 output features (224 workgroups); wave w sums
-// over inputs 4096 w .. 4096 w + 4095 (256 steps of 16) and the four partial
-// sums are added through LDS.  M = o (wo rows, 16-byte loads straight into the
-// MFMA A layout: lane l takes row l % 32, inputs 8 (l / 32) .. + 7 of the
-// step), N = b (x rows, B layout, rows past B repeat row B - 1 and are not
-// stored), K = i.  The loads of step group g (U = 4 steps) are issued D = 4
-// groups ahead into register rings, in the order they are needed, so the
-// in-order wait for group g never covers a later group.
+// HBM-bound on wo (235 MB, read once per launch of up to 64 batch rows).
+// Workgroup = 28 output features (7168 = 256 x 28: one workgroup per CU),
+// padded to the 32 rows of an MFMA tile (rows past 28 lie outside the weight
+// range and load zeros).  K = i is walked in chunks of 256; wave w takes
+// line w of every chunk (its 64 columns: K-steps 4w .. 4w + 3), so each
+// wave moves, by whole-line LDS-DMA into three buffers of its own, exactly
+// the 128-byte lines it reads: the 32 wo rows' and the x rows' line w of
+// the chunk, two chunks ahead.  The waves never wait for each other until
+// the end, where their sums are added through LDS.  Line of row r at
+// segment r (wo) or 32 + r (x) of a buffer, 16-byte chunk q at position
+// q ^ seg_swz(r): the fragment reads of 32 rows at one chunk hit distinct
+// banks.  M = o (A fragments), N = b (B fragments), K = i.  Each CU ingests
+// all of x (2 MB at B = 64, twice its 0.9 MB of wo), which with two chunks
+// in flight per wave is what sets the rate at large batches.
 // ---------------------------------------------------------------------------
+constexpr int kOpRows = 28;        // output features per workgroup
+constexpr int kOpChunk = 256;      // K per chunk: four 64-column lines
+
 template <int NT>
 __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a) {
-  constexpr int U = 4, D = 4, G = (kWoIn / 4) / (16 * U);  // 64 groups per wave
-  __shared__ float red[4][NT][64][16];
-  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  constexpr int XR = 32 * NT;                    // x rows staged per chunk
+  constexpr int kSegs = 32 + XR;                 // 128-byte segments per buffer
+  constexpr int kWaveLds = 3 * kSegs * 128;      // three buffers per wave
+  constexpr int kDpc = 4 + XR / 8;               // DMA instructions per wave per chunk
+  constexpr int kChunks = kWoIn / kOpChunk;      // 64
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kWaveLds];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = 32 * (int)blockIdx.x;
-  const int k0 = (kWoIn / 4) * wave + 8 * hh;
-  const uint16_t* pa = a.wo + (size_t)(n0 + r) * kWoIn + k0;
-  const uint16_t* pb[NT];
+  const int o0 = kOpRows * (int)blockIdx.x;
+  char LDS_AS* wl = (char LDS_AS*)smem + wave * kWaveLds;
+  const uint32_t lds_w = (uint32_t)(uintptr_t)wl;
+  const i32x4 rw = buffer_rsrc(a.wo + (size_t)o0 * kWoIn, (uint32_t)(kOpRows * kWoIn * 2));
+  const i32x4 rx = buffer_rsrc(a.x, (uint32_t)(((int64_t)(a.B - 1) * a.x_sb + kWoIn) * 2));
+  const uint32_t r8 = (uint32_t)(lane >> 3);
+  // Chunk c into buffer c % 3: instruction j moves rows 8j .. 8j + 7 (lane l:
+  // row 8j + l / 8, position l % 8, source chunk (l % 8) ^ seg_swz(row)).
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const uint32_t buf = lds_w + (uint32_t)((c % 3) * kSegs * 128);
+    const uint32_t col = (uint32_t)(c * kOpChunk + 64 * wave) * 2u;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) pb[t] = a.x + (int64_t)min(32 * t + r, a.B - 1) * a.x_sb + k0;
-  bf16x8 ra[D][U], rb[D][U][NT];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t r = (uint32_t)(8 * j) + r8;
+      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
+      dma16(rw, buf + (uint32_t)(8 * j) * 128u, r * (uint32_t)(kWoIn * 2) + col + q16);
+    }
+#pragma unroll
+    for (int j = 0; j < XR / 8; ++j) {
+      const uint32_t r = (uint32_t)(8 * j) + r8;
+      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
+      dma16(rx, buf + (uint32_t)(32 + 8 * j) * 128u, r * (uint32_t)(a.x_sb * 2) + col + q16);
+    }
+  };
+  // Fragment of K-step t (0..3) of the wave's line: row `row` of segment
+  // base `seg0`, chunk 2 t + hh.
+  const uint32_t r32 = (uint32_t)(lane & 31);
+  auto frag = [&](const char LDS_AS* buf, uint32_t seg0, int t) __attribute__((always_inline)) {
+    const uint32_t q = (uint32_t)(2 * t + hh);
+    return *(const bf16x8 LDS_AS*)(buf + (seg0 + r32) * 128u + ((q ^ seg_swz(r32)) * 16u));
+  };
+
   f32x16 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
-  auto load = [&](int g, int d) __attribute__((always_inline)) {
+  issue(0);
+  issue(1);
+  for (int c = 0; c < kChunks; ++c) {
+    // Chunk c has landed when at most chunk c + 1's loads are outstanding.
+    if (c + 1 < kChunks) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDpc) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Buffer (c + 2) % 3 last held chunk c - 1, whose fragments were read
+    // (and used) in the previous iteration.
+    if (c + 2 < kChunks) issue(c + 2);
+    const char LDS_AS* buf = wl + (c % 3) * kSegs * 128;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      ra[d][u] = ld8(pa + 16 * (U * g + u));
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 af = frag(buf, 0u, t);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) rb[d][u][t] = ld8(pb[t] + 16 * (U * g + u));
-    }
-  };
-  auto mma = [&](int d) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mfma32(ra[d][u], rb[d][u][t], acc[t]);
-  };
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, d);
-  for (int g0 = 0; g0 < G - D; g0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      mma(d);
-      load(g0 + D + d, d);
+      for (int n = 0; n < NT; ++n) acc[n] = mfma32(af, frag(buf, (uint32_t)(32 + 32 * n), t), acc[n]);
     }
   }
-#pragma unroll
-  for (int d = 0; d < D; ++d) mma(d);
 
-  // acc[t][v] of lane l: output feature n0 + 8 (v / 4) + 4 (l / 32) + v % 4,
-  // batch row 32 t + l % 32.
+  // acc[n][v] of lane l: output feature o0 + 8 (v / 4) + 4 (l / 32) + v % 4,
+  // batch row 32 n + l % 32.  Each wave's sums into its own LDS region, then
+  // every thread adds the four waves' values of 8 outputs.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float* red = reinterpret_cast<float*>(smem + wave * kWaveLds);
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) red[wave][t][lane][v] = acc[t][v];
+    for (int v = 0; v < 16; ++v) red[(n * 16 + v) * 64 + lane] = acc[n][v];
   __syncthreads();
-  for (int e = tid; e < NT * 64 * 16; e += 256) {
-    const int t = e >> 10, l = (e >> 4) & 63, v = e & 15;
-    const float sum = red[0][t][l][v] + red[1][t][l][v] + red[2][t][l][v] + red[3][t][l][v];
-    const int b = 32 * t + (l & 31);
-    if (b < a.B)
-      a.out[(int64_t)b * a.out_sb + n0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3)] = __builtin_bit_cast(uint16_t, (__bf16)sum);
+  for (int e = tid; e < NT * 16 * 64; e += 256) {
+    const int n = e >> 10, v = (e >> 6) & 15, l = e & 63;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sum += reinterpret_cast<const float*>(smem + w * kWaveLds)[e];
+    const int m = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    const int b = 32 * n + (l & 31);
+    if (m < kOpRows && b < a.B)
+      a.out[(int64_t)b * a.out_sb + o0 + m] = __builtin_bit_cast(uint16_t, (__bf16)sum);
   }
 }
 
@@ -1465,7 +1500,8 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 }
 
 int launch_output_proj(const OutProjArgs& a, void* stream) {
-  const dim3 grid(kWoOut / 32);
+  static_assert(kWoOut % kOpRows == 0, "whole output tiles");
+  const dim3 grid(kWoOut / kOpRows);
   if (a.B <= 32) hipLaunchKernelGGL(output_proj_kernel<1>, grid, dim3(256), 0, (hipStream_t)stream, a);
   else hipLaunchKernelGGL(output_proj_kernel<2>, grid, dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
