@@ -299,6 +299,26 @@ def main():
     torch.cuda.synchronize()
     warm_ms = start.elapsed_time(end) / args.steps
     last_set = sets[0]
+    # Steady state, labelled as such: the same rotated steps run continuously
+    # for at least 50 ms first (under sustained load the GPU runs a few
+    # milliseconds fast, then ~10 % slow for about ten milliseconds, then
+    # settles), then five trials of K steps without a pause between them.
+    t_end = time.perf_counter() + 0.05
+    i = 0
+    while time.perf_counter() < t_end:
+        launchers[i % R]()
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record(stream)
+    for t in range(5):
+        for i in range(args.steps):
+            launchers[i % R]()
+        ev[t + 1].record(stream)
+    torch.cuda.synchronize()
+    steady = [ev[t].elapsed_time(ev[t + 1]) / args.steps for t in range(5)]
+    steady_ms = sorted(steady)[2]
     # Pass 2 (kernel time for the roofline): K decode launches back to back on
     # the same stream, cycling the input sets, bracketed by two HIP events.
     # An event pair around every launch would add ~3 us to each; back to
@@ -414,7 +434,8 @@ def main():
         prefill = prefill_pass(args, mla, workload, torch, stream)
     log(f"{args.steps} steps x 5 trials: " + ", ".join(f"{t * 1e3:.2f}" for t in trials) +
         f" us/step (median {ms_step * 1e3:.2f}); host enqueue " + ", ".join(f"{t * 1e6:.1f}" for t in enqueue) +
-        f" us/step; warm (no rotation) {warm_ms * 1e3:.2f} us; decode kernel {decode_ms * 1e3:.2f} us, "
+        f" us/step; steady state {steady_ms * 1e3:.2f} us; warm (no rotation) {warm_ms * 1e3:.2f} us; "
+        f"decode kernel {decode_ms * 1e3:.2f} us, "
         f"decode + combine {attn_ms * 1e3:.2f} us; plan splits={bufs.num_splits}")
 
     # Algorithmic work per step: the mean over the K steps of a trial (step i
@@ -516,6 +537,9 @@ def main():
         "trials_us_per_step": [t * 1e3 for t in trials],
         "value_from": "median of the 5 trials",
         "host_enqueue_us_per_step": [t * 1e6 for t in enqueue],
+        "steady_state": {"value": B / (steady_ms * 1e-3), "unit": "queries/s", "us_per_step": steady_ms * 1e3,
+                         "trials_us_per_step": [t * 1e3 for t in steady],
+                         "note": "median of five trials of the same rotated steps after >= 50 ms of continuous steps"},
         "warm_no_rotation": {"value": B / (warm_ms * 1e-3), "unit": "queries/s", "us_per_step": warm_ms * 1e3,
                              "note": "input set 0 every step (cache-warm; not the headline)"},
         "attention_only": {"value": B / (attn_ms * 1e-3), "unit": "queries/s", "us": attn_ms * 1e3,
