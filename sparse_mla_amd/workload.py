@@ -32,9 +32,9 @@ class Spec:
 
     lens: "fixed" (every L_b = L) or "ragged" (L_b uniform in [lo, L]).
     select: "dense" (no index list: every position), "uniform" (k distinct
-    positions uniformly without replacement) or "recent" (the most recent 512
-    positions plus k-512 drawn uniformly from the rest; every position when
-    L_b <= k).
+    positions uniformly without replacement) or "recent" (the most recent
+    w = min(512, k/4) positions plus k-w drawn uniformly from the rest, in
+    shuffled order; every position when L_b <= k).
     """
     name: str
     B: int
@@ -137,8 +137,9 @@ def _indices(spec: Spec, lens: torch.Tensor, k: int, seed: int) -> torch.Tensor:
             if Lb <= k:
                 r = torch.randperm(Lb, generator=g)
             else:
-                recent = torch.arange(Lb - 512, Lb)
-                rest = torch.randperm(Lb - 512, generator=g)[: k - 512]
+                w = min(512, k // 4)
+                recent = torch.arange(Lb - w, Lb)
+                rest = torch.randperm(Lb - w, generator=g)[: k - w]
                 both = torch.cat([recent, rest])
                 r = both[torch.randperm(k, generator=g)]
         else:
