@@ -359,6 +359,25 @@ int mla_combine_value_up_fp8(const void* workspace, size_t ws_bytes, int32_t B, 
 int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
                     void* stream);
 
+/*
+ * The output projection on a repacked weight (the same "Attention update"
+ * passage; a layout of the same linear weight, made once at set-up like the
+ * fp8 dequantisation).  mla_output_proj reads, per chunk of 256 inputs, a
+ * 512-byte piece of each of 7168 weight rows 32 KB apart; the packed layout
+ * stores each group of 28 output rows chunk by chunk, so the same bytes are
+ * read as one contiguous stream per group (measured about 10 % faster at batches
+ * up to 32; no change at 64, where reading x sets the pace).
+ *   mla_output_proj_pack: wo_packed[g][c][r][k] = wo[28 g + r][256 c + k]
+ *     for g < 256, c < 64, r < 28, k < 256; wo and wo_packed bf16, 7168 x 16384
+ *     elements each (235 MB), 16-byte aligned, not overlapping.
+ *   mla_output_proj_packed: arguments, results and errors as
+ *     mla_output_proj, with wo_packed from mla_output_proj_pack; the result
+ *     is bit-identical to mla_output_proj on the unpacked weight.
+ */
+int mla_output_proj_pack(const void* wo, void* wo_packed, void* stream);
+int mla_output_proj_packed(const void* x, int64_t x_sb, const void* wo_packed, void* out, int64_t out_sb,
+                           int32_t B, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

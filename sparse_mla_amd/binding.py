@@ -91,6 +91,8 @@ _value_up_fp8 = _sig("mla_value_up_fp8", ctypes.c_int, [_p, _p, _p, _p, _i64, _i
 _combine_value_up_fp8 = _sig("mla_combine_value_up_fp8", ctypes.c_int,
                              [_p, _sz, _i32, _i32, _p, _p, _p, _i64, _i64, _p, _p, _p])
 _output_proj = _sig("mla_output_proj", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p])
+_output_proj_pack = _sig("mla_output_proj_pack", ctypes.c_int, [_p, _p, _p])
+_output_proj_packed = _sig("mla_output_proj_packed", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p])
 MODEL_DIM = 7168
 
 
@@ -373,11 +375,7 @@ def mla_combine_value_up(workspace, B: int, num_splits: int, wkv_b: torch.Tensor
     return out
 
 
-def mla_output_proj(x: torch.Tensor, wo: torch.Tensor, out: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
-    """x: the value-up output, bf16 [B, 1, 128, 128] or [B, 16384] (each row's
-    16384 values contiguous); wo: bf16 [7168, 16384], contiguous.  Returns
-    out bf16 [B, 1, 7168] (or writes `out`, [B, 1, 7168] or [B, 7168])."""
+def _output_proj_args(x, wo, out):
     _need(x, "x", torch.bfloat16)
     _need(wo, "wo", torch.bfloat16, 2)
     B = x.shape[0]
@@ -392,8 +390,42 @@ def mla_output_proj(x: torch.Tensor, wo: torch.Tensor, out: Optional[torch.Tenso
     of = out.reshape(B, -1)
     if of.shape[1] != MODEL_DIM or of.stride(1) != 1 or of.data_ptr() != out.data_ptr():
         raise ValueError("out must be [B, 1, 7168] or [B, 7168] with contiguous rows")
-    _check("mla_output_proj", _output_proj(_ptr(x), xf.stride(0), _ptr(wo), _ptr(out), of.stride(0), B,
-                                           _stream(stream)))
+    return B, xf.stride(0), out, of.stride(0)
+
+
+def mla_output_proj(x: torch.Tensor, wo: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """x: the value-up output, bf16 [B, 1, 128, 128] or [B, 16384] (each row's
+    16384 values contiguous); wo: bf16 [7168, 16384], contiguous.  Returns
+    out bf16 [B, 1, 7168] (or writes `out`, [B, 1, 7168] or [B, 7168])."""
+    B, x_sb, out, out_sb = _output_proj_args(x, wo, out)
+    _check("mla_output_proj", _output_proj(_ptr(x), x_sb, _ptr(wo), _ptr(out), out_sb, B, _stream(stream)))
+    return out
+
+
+def mla_output_proj_pack(wo: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The output-projection weight repacked for mla_output_proj_packed (one-time
+    set-up): a bf16 tensor of wo's shape holding the same values in groups of
+    28 rows stored chunk by chunk."""
+    _need(wo, "wo", torch.bfloat16, 2)
+    if tuple(wo.shape) != (MODEL_DIM, HEADS * VALUE) or not wo.is_contiguous():
+        raise ValueError("wo must be a contiguous [7168, 16384] tensor")
+    if out is None:
+        out = torch.empty_like(wo)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != tuple(wo.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [7168, 16384] tensor")
+    _check("mla_output_proj_pack", _output_proj_pack(_ptr(wo), _ptr(out), _stream(stream)))
+    return out
+
+
+def mla_output_proj_packed(x: torch.Tensor, wo_packed: torch.Tensor, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """mla_output_proj with the weight from mla_output_proj_pack (bit-identical
+    result)."""
+    B, x_sb, out, out_sb = _output_proj_args(x, wo_packed, out)
+    _check("mla_output_proj_packed", _output_proj_packed(_ptr(x), x_sb, _ptr(wo_packed), _ptr(out), out_sb, B,
+                                                         _stream(stream)))
     return out
 
 

@@ -502,8 +502,8 @@ int mla_value_up_fp8(const void* o_latent, const void* w_fp8, const float* w_sca
   return value_up_impl(o_latent, nullptr, f, out, out_sb, out_sh, B, stream);
 }
 
-int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
-                    void* stream) {
+static int output_proj_impl(const void* x, int64_t x_sb, const void* wo, bool packed, void* out, int64_t out_sb,
+                            int32_t B, void* stream) {
   if (!x || !wo || !out) return MLA_ERR_NULL_POINTER;
   if (B < 1 || B > 65536 || x_sb < mla::kWoIn || out_sb < mla::kWoOut) return MLA_ERR_BAD_DIM;
   if (!aligned16(x) || !aligned16(wo) || !stride8(x_sb) || (reinterpret_cast<uintptr_t>(out) & 1u) != 0)
@@ -518,10 +518,28 @@ int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int6
     a.x_sb = x_sb;
     a.out_sb = out_sb;
     a.B = B - b0 < 64 ? B - b0 : 64;
+    a.packed = packed;
     const int st = hip_status(mla::launch_output_proj(a, stream));
     if (st != MLA_OK) return st;
   }
   return MLA_OK;
+}
+
+int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
+                    void* stream) {
+  return output_proj_impl(x, x_sb, wo, false, out, out_sb, B, stream);
+}
+
+int mla_output_proj_pack(const void* wo, void* wo_packed, void* stream) {
+  if (!wo || !wo_packed) return MLA_ERR_NULL_POINTER;
+  if (!aligned16(wo) || !aligned16(wo_packed)) return MLA_ERR_ALIGNMENT;
+  return hip_status(mla::launch_output_proj_pack(static_cast<const uint16_t*>(wo),
+                                                 static_cast<uint16_t*>(wo_packed), stream));
+}
+
+int mla_output_proj_packed(const void* x, int64_t x_sb, const void* wo_packed, void* out, int64_t out_sb,
+                           int32_t B, void* stream) {
+  return output_proj_impl(x, x_sb, wo_packed, true, out, out_sb, B, stream);
 }
 
 int mla_combine_value_up(const void* workspace, size_t ws_bytes, int32_t B, int32_t num_splits,

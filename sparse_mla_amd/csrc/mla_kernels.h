@@ -107,6 +107,7 @@ struct OutProjArgs {
   uint16_t* out;        // [B][out_sb], the first kWoOut values of each row written
   int64_t x_sb, out_sb;
   int32_t B;            // 1 .. 64
+  bool packed;          // wo in the layout written by launch_output_proj_pack
 };
 
 // Each returns a hipError_t value (0 on success).
@@ -116,6 +117,7 @@ int launch_combine(const CombineArgs& a, void* stream);
 int launch_value_up(const ValueUpArgs& a, void* stream);  // fused combine when o_latent == NULL
 int launch_dequant(const DequantArgs& a, void* stream);
 int launch_output_proj(const OutProjArgs& a, void* stream);
+int launch_output_proj_pack(const uint16_t* wo, uint16_t* packed, void* stream);
 int device_cu_count(int* cus);
 
 // Static device scratch of mla_sparse_decode_noalloc: kScratchBytes per GPU.

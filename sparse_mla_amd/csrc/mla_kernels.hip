@@ -1367,7 +1367,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
 constexpr int kOpRows = 28;        // output features per workgroup
 constexpr int kOpChunk = 256;      // K per chunk: four 64-column lines
 
-template <int NT>
+// PACKED: wo in the layout of mla_output_proj_pack, where workgroup g's 28
+// rows are stored chunk by chunk ([chunk][row][256 columns]), so that each
+// chunk's weight lines are one contiguous 14 KB piece; the same bytes reach
+// the same LDS slots either way.
+template <int NT, bool PACKED>
 __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a) {
   constexpr int XR = 32 * NT;                    // x rows staged per chunk
   constexpr int kSegs = 32 + XR;                 // 128-byte segments per buffer
@@ -1392,7 +1396,12 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
     for (int j = 0; j < 4; ++j) {
       const uint32_t r = (uint32_t)(8 * j) + r8;
       const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
-      dma16(rw, buf + (uint32_t)(8 * j) * 128u, r * (uint32_t)(kWoIn * 2) + col + q16);
+      const uint32_t off = PACKED ? (r < (uint32_t)kOpRows
+                                         ? ((uint32_t)c * kOpRows + r) * (uint32_t)(kOpChunk * 2) +
+                                               (uint32_t)(128 * wave) + q16
+                                         : kMaskedOffset)
+                                  : r * (uint32_t)(kWoIn * 2) + col + q16;
+      dma16(rw, buf + (uint32_t)(8 * j) * 128u, off);
     }
 #pragma unroll
     for (int j = 0; j < XR / 8; ++j) {
@@ -1453,6 +1462,24 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
 }
 
 // ---------------------------------------------------------------------------
+// Output-projection weight repack (one-time set-up): packed[g][c][r][k] =
+// wo[28 g + r][256 c + k] for the 256 workgroups g, 64 chunks c, 28 rows r
+// and 256 columns k, 16 bytes per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void output_proj_pack_kernel(const uint16_t* __restrict__ wo,
+                                                               uint16_t* __restrict__ packed) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;  // packed element index
+  const int k = (int)(i % kOpChunk);
+  const size_t rest = i / kOpChunk;
+  const int r = (int)(rest % kOpRows);
+  const size_t gc = rest / kOpRows;
+  const int c = (int)(gc % (kWoIn / kOpChunk));
+  const int g = (int)(gc / (kWoIn / kOpChunk));
+  const size_t src = (size_t)(kOpRows * g + r) * kWoIn + (size_t)c * kOpChunk + k;
+  *reinterpret_cast<uint4*>(packed + i) = *reinterpret_cast<const uint4*>(wo + src);
+}
+
+// ---------------------------------------------------------------------------
 // fp8 dequantisation (one-time set-up): the whole weight, with the helpers
 // above.
 // ---------------------------------------------------------------------------
@@ -1502,8 +1529,22 @@ int launch_decode(const DecodeArgs& a, void* stream) {
 int launch_output_proj(const OutProjArgs& a, void* stream) {
   static_assert(kWoOut % kOpRows == 0, "whole output tiles");
   const dim3 grid(kWoOut / kOpRows);
-  if (a.B <= 32) hipLaunchKernelGGL(output_proj_kernel<1>, grid, dim3(256), 0, (hipStream_t)stream, a);
-  else hipLaunchKernelGGL(output_proj_kernel<2>, grid, dim3(256), 0, (hipStream_t)stream, a);
+  const hipStream_t st = (hipStream_t)stream;
+  if (a.packed) {
+    if (a.B <= 32) hipLaunchKernelGGL((output_proj_kernel<1, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((output_proj_kernel<2, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (a.B <= 32) hipLaunchKernelGGL((output_proj_kernel<1, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((output_proj_kernel<2, false>), grid, dim3(256), 0, st, a);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_output_proj_pack(const uint16_t* wo, uint16_t* packed, void* stream) {
+  constexpr size_t n = (size_t)kWoOut * kWoIn;
+  static_assert(n % (256 * 8) == 0, "whole workgroups");
+  hipLaunchKernelGGL(output_proj_pack_kernel, dim3((unsigned)(n / (256 * 8))), dim3(256), 0, (hipStream_t)stream,
+                     wo, packed);
   return (int)hipGetLastError();
 }
 

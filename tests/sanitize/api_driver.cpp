@@ -26,6 +26,7 @@ int launch_combine(const CombineArgs& a, void*) { last_combine = a; ++n_launch; 
 int launch_value_up(const ValueUpArgs& a, void*) { last_vu = a; ++n_launch; return 0; }
 int launch_dequant(const DequantArgs&, void*) { ++n_launch; return 0; }
 int launch_output_proj(const OutProjArgs& a, void*) { last_oproj = a; ++n_launch; return 0; }
+int launch_output_proj_pack(const uint16_t*, uint16_t*, void*) { ++n_launch; return 0; }
 int device_cu_count(int* cus) { *cus = 256; return 0; }
 static char fake_scratch[256] __attribute__((aligned(256)));
 int scratch_buffer(void** ptr) { *ptr = fake_scratch; return 0; }
@@ -110,6 +111,11 @@ int main() {
   CHECK(mla_output_proj(P(F), 16384, P(F), P(F), 7168, 100, nullptr) == MLA_OK && mla::n_launch == b0 + 2);
   CHECK(mla::last_oproj.B == 36);
   CHECK(mla_output_proj(P(F), (int64_t)1 << 26, P(F), P(F), 7168, 4, nullptr) == MLA_ERR_RANGE);
+  CHECK(!mla::last_oproj.packed);
+  CHECK(mla_output_proj_packed(P(F), 16384, P(F), P(F), 7168, 70, nullptr) == MLA_OK && mla::last_oproj.packed &&
+        mla::last_oproj.B == 6);
+  CHECK(mla_output_proj_pack(P(F), P(F + 16), nullptr) == MLA_OK);
+  CHECK(mla_output_proj_pack(P(F), P(F + 2), nullptr) == MLA_ERR_ALIGNMENT);
   for (int code = 0; code <= 8; ++code) CHECK(mla_status_string(code) != nullptr);
   puts("api sanitizer driver: ok");
   return 0;

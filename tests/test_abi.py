@@ -33,6 +33,8 @@ def lib():
     L.mla_combine_value_up.argtypes = [p, sz, i32, i32, p, p, i64, i64, p, p, p]
     L.mla_dequant_wkv_b_fp8.argtypes = [p, p, p, p]
     L.mla_output_proj.argtypes = [p, i64, p, p, i64, i32, p]
+    L.mla_output_proj_packed.argtypes = [p, i64, p, p, i64, i32, p]
+    L.mla_output_proj_pack.argtypes = [p, p, p]
     L.mla_workspace_bytes.restype = sz
     L.mla_workspace_bytes.argtypes = [i32, i32]
     L.mla_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32)]
@@ -198,6 +200,19 @@ def test_output_proj_host_checks(lib):
     assert lib.mla_output_proj(a, 16388, a, a, 7168, 4, None) == ALIGN     # stride not a multiple of 8
     assert lib.mla_output_proj(a, 16384, a + 8, a, 7168, 4, None) == ALIGN
     assert lib.mla_output_proj(a, 16384, a, a + 1, 7168, 4, None) == ALIGN
+
+
+def test_output_proj_packed_host_checks(lib):
+    a = 1 << 20
+    assert lib.mla_output_proj_pack(None, a, None) == NULLP
+    assert lib.mla_output_proj_pack(a, None, None) == NULLP
+    assert lib.mla_output_proj_pack(a + 8, a, None) == ALIGN
+    assert lib.mla_output_proj_pack(a, a + 2, None) == ALIGN
+    f = lib.mla_output_proj_packed
+    assert f(None, 16384, a, a, 7168, 4, None) == NULLP
+    assert f(a, 16384, a, a, 7168, 0, None) == BADDIM
+    assert f(a, 16384, a + 8, a, 7168, 4, None) == ALIGN
+    assert f(a, 1 << 26, a, a, 7168, 4, None) == RANGE
 
 
 def test_noalloc_host_checks(lib):

@@ -2,7 +2,10 @@
 "Attention update" page, mla-output) against the fp64 oracle on sampled
 batch rows: within 1e-2 * max|ref| (fp32 accumulation over 16384 products,
 one rounding to bf16), across one and two 32-row batch tiles, a batch split
-over two launches (64 + 36 rows), and strided input and output rows."""
+over two launches (64 + 36 rows), and strided input and output rows.  The
+repacked weight (mla_output_proj_pack) is checked element for element against
+its definition, and mla_output_proj_packed bit for bit against
+mla_output_proj on the unpacked weight."""
 import numpy as np
 import pytest
 import torch
@@ -49,3 +52,24 @@ def test_output_proj_strided_rows(mla, inputs):
     ref = oracle.output_proj(x[rows], wo)
     assert rel_err(f64(big)[rows, :7168], ref) <= REL_TOL
     assert torch.all(big[:, 7168:] == 7.0)  # nothing written past each row's 7168 values
+
+
+def test_output_proj_pack_layout(mla, inputs):
+    _, _, _, wog = inputs
+    packed = mla.mla_output_proj_pack(wog)
+    torch.cuda.synchronize()
+    # packed[g][c][r][k] = wo[28 g + r][256 c + k]
+    ref = wog.view(256, 28, 64, 256).permute(0, 2, 1, 3).contiguous().view(7168, 16384)
+    assert torch.equal(packed.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [1, 9, 32, 33, 64, 100])
+def test_output_proj_packed_bit_identical(mla, inputs, B):
+    x, wo, xg, wog = inputs
+    packed = mla.mla_output_proj_pack(wog)
+    a = mla.mla_output_proj(xg[:B], wog)
+    b = mla.mla_output_proj_packed(xg[:B], packed)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.output_proj(x[[0, B - 1]], wo)
+    assert rel_err(f64(b)[[0, B - 1], 0], ref) <= REL_TOL
