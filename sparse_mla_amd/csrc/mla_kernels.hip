@@ -775,7 +775,8 @@ constexpr int kOffQ = kBufBytes;
 constexpr int kQWave = 7 * kBlk * 128;
 constexpr int kOffIdx = kOffQ + 4 * kQWave;  // int [kIdxCap]
 constexpr int kOffLen = kOffIdx + kIdxCap * 4;  // int [4][64]: the sequence length, per wave
-constexpr int kDecodeLds = kOffLen + 4 * 64 * 4;
+constexpr int kOffTot = kOffLen + 4 * 64 * 4;   // int [4]: valid slots per wave (compaction)
+constexpr int kDecodeLds = kOffTot + 4 * 4;
 constexpr int kSoftSteps = 32;              // softmax steps placed beside MFMAs
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
 constexpr int kTilePitch = 1040;            // output tile row: 512 bf16 + 16 bytes of padding
@@ -789,18 +790,34 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   char LDS_AS* s3 = (char LDS_AS*)smem;
   int* sidx = reinterpret_cast<int*>(smem + kOffIdx);
 
-  // Units (sequence, split) are numbered so that the splits of a sequence
-  // run on one XCD (workgroup x is dispatched to XCD x % 8): the sequence's
-  // query tile then comes from HBM once and from that XCD's L2 after.
-  const int units = a.B * a.S;
-  const int per_xcd = (units + 7) >> 3;
-  const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (unit >= units) return;
-  const int b = unit / a.S, s = unit % a.S;
+  // Units (row, split) are numbered so that the splits of a row run on one
+  // XCD (workgroup x is dispatched to XCD x % 8): the row's query tile then
+  // comes from HBM once and from that XCD's L2 after.
   // Prefill: row b is query token b % T of prompt b / T, whose keys are the
   // prompt's own positions (one cache per prompt), causally limited to the
   // token's own position.  Decode: row b is sequence b.
   const bool causal = a.causal != 0;
+  int b, s;
+  if (!causal) {
+    // Each XCD takes a contiguous range of units.
+    const int units = a.B * a.S;
+    const int per_xcd = (units + 7) >> 3;
+    const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (unit >= units) return;
+    b = unit / a.S;
+    s = unit % a.S;
+  } else {
+    // A token's work grows with its position (its masked slots cost no
+    // blocks), so rows are dealt to the XCDs in turn, latest tokens first:
+    // every XCD gets an even share and the longest workgroups start first.
+    // Dispatch-order row j (the XCD's (i / S)-th, i its workgroup count on
+    // that XCD) is token T - 1 - j / P of prompt j % P (P prompts).
+    const int j = (int)(blockIdx.x >> 3) / a.S * 8 + (int)(blockIdx.x & 7);
+    if (j >= a.B) return;
+    const int T = a.rows_per_seq, P = a.B / a.rows_per_seq;
+    b = (j % P) * T + (T - 1 - j / P);
+    s = (int)(blockIdx.x >> 3) % a.S;
+  }
   const int seq = causal ? b / a.rows_per_seq : b;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -812,7 +829,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const int s0 = s * a.chunk;
   const int s1 = min(a.k_max, s0 + a.chunk);
   const int nslot = max(0, s1 - s0);
-  const int nblk = (nslot + kBlk - 1) / kBlk;
+  // Slots actually walked, decided once the length and the index list are in
+  // (below): unless the scores of every slot are requested, the valid slots
+  // of an index list are moved to its front and a dense split stops at L_b,
+  // so masked slots cost no blocks.
+  int nkeys = nslot;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)s3;
   // Score-read offsets: row lane % 32 of a tile laid out like a gathered
@@ -892,11 +913,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
 
   // Stage this split's index slots as cache rows (-1 = masked).  The same
   // predicate decides validity, the attended bitmap and the device checks.
+  const bool keep_slots = (a.flags & 2u) != 0;  // per-slot scores: slot order kept
   if constexpr (!dense) {
     {
       const int i0 = 4 * tid;
       const int4 raw = *reinterpret_cast<const int4*>(sidx + i0);
       int r[4] = {raw.x, raw.y, raw.z, raw.w};
+      int cnt = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = r[e];
@@ -912,8 +935,40 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
           }
         }
         r[e] = ok ? t : -1;
+        cnt += ok ? 1 : 0;
       }
-      *reinterpret_cast<int4*>(sidx + i0) = make_int4(r[0], r[1], r[2], r[3]);
+      if (keep_slots) {
+        *reinterpret_cast<int4*>(sidx + i0) = make_int4(r[0], r[1], r[2], r[3]);
+      } else {
+        // Stable compaction: the valid slots, in slot order, to the front.
+        // This thread's place = the valid slots of the threads before it:
+        // within the wave from the three bit planes of cnt (0 .. 4), across
+        // waves from the per-wave totals in LDS.
+        const uint64_t p0 = __builtin_amdgcn_ballot_w64((cnt & 1) != 0);
+        const uint64_t p1 = __builtin_amdgcn_ballot_w64((cnt & 2) != 0);
+        const uint64_t p2 = __builtin_amdgcn_ballot_w64((cnt & 4) != 0);
+        auto below = [&](uint64_t m) __attribute__((always_inline)) {
+          return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        };
+        const int before = below(p0) + 2 * below(p1) + 4 * below(p2);
+        int* stot = reinterpret_cast<int*>(smem + kOffTot);
+        if (lane == 0) stot[wave] = __popcll(p0) + 2 * __popcll(p1) + 4 * __popcll(p2);
+        __syncthreads();  // the totals are in; every thread holds its raw slots
+        int base = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int tw = stot[w];
+          base += w < wave ? tw : 0;
+          total += tw;
+        }
+        int pos = base + before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (r[e] >= 0) sidx[pos++] = r[e];
+        // The last block's slots past the valid ones are masked.
+        for (int i = total + tid; i < ((total + kBlk - 1) & ~(kBlk - 1)); i += 256) sidx[i] = -1;
+        nkeys = total;
+      }
     }
   } else {
     if (validate) {
@@ -922,7 +977,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
         if (t < Lb) atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), 1u << (t & 31));
       }
     }
+    // Positions from L_b on are masked: the split stops there.
+    if (!keep_slots) nkeys = max(0, min(nslot, Lb - s0));
   }
+  const int nblk = __builtin_amdgcn_readfirstlane((nkeys + kBlk - 1) / kBlk);
   // Every wave has read its query lines 7 and 8 out of buffer 0 before this
   // barrier, after which block 0 is gathered there.
 #pragma unroll
@@ -1518,8 +1576,9 @@ int launch_absorb(const AbsorbArgs& a, void* stream) {
 
 int launch_decode(const DecodeArgs& a, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
-  const int units = a.B * a.S;
-  const int grid = 8 * ((units + 7) / 8);  // whole XCD rounds; spare workgroups exit
+  // Whole XCD rounds; spare workgroups exit.  Prefill deals whole rows (all
+  // their splits) to each XCD in turn.
+  const int grid = a.causal ? 8 * ((a.B + 7) / 8) * a.S : 8 * ((a.B * a.S + 7) / 8);
   auto* k = a.indices == nullptr ? (a.S > 1 ? decode_kernel<true, true> : decode_kernel<true, false>)
                                   : (a.S > 1 ? decode_kernel<false, true> : decode_kernel<false, false>);
   hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, st, a);

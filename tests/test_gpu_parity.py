@@ -206,3 +206,65 @@ def test_decode_deterministic_and_order_invariant(mla):
     _, out3 = _run_decode(mla, g, 2)
     ref = oracle_ref(w)
     assert rel_err(f64(out3)[:, 0], ref["out"]) <= REL_TOL
+
+
+def _split_chunk(k_max, S):
+    c = -(-k_max // S)
+    return -(-c // 32) * 32
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_decode_masked_slots_compacted(mla, S):
+    """Slots that select nothing (-1 padding, a negative value, values past
+    the sequence) scattered through every row, and with several splits one
+    split of a row holding none at all: unless per-slot scores are requested
+    the kernel moves each split's valid slots to its front and walks only
+    their blocks.  O~, O and the LSE match the oracle on the same selection
+    (invalid slots given to it as -1), the row sums hold, the attended bitmap
+    and the out-of-range status are exact, and the result equals the
+    slot-order path (per-slot scores requested) up to rounding."""
+    w = workload.make("sparse_b32_l4096_k2048", B=5, L=300, k=200)
+    gen = torch.Generator().manual_seed(41)
+    idx = w.indices.clone()
+    idx[torch.rand(idx.shape, generator=gen) < 0.5] = -1
+    past = (torch.rand(idx.shape, generator=gen) < 0.05) & (idx == -1)
+    idx[past] = 100000                      # past every length: masked, flagged
+    idx[0, 10] = -7                         # negative and not -1: masked, flagged
+    if S > 1:
+        idx[2, :_split_chunk(200, S)] = -1   # split 0 of row 2 selects nothing
+    clean = idx.clone()
+    clean[(clean < 0) | (clean >= 300)] = -1
+    w.indices = idx
+    g = to_gpu(w)
+    words = (w.max_len + 31) // 32
+    bitmap = torch.zeros((w.B, words), dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs, out = _run_decode(mla, g, S, flags=mla.MLA_FLAG_VALIDATE, bitmap=bitmap, status=status)
+    o_lat, lse = f64(bufs.o_latent), f64(bufs.lse)
+    scores = torch.empty((w.B, 128, w.k_max), dtype=torch.float32, device="cuda")
+    bufs2, out2 = _run_decode(mla, g, S, flags=mla.MLA_FLAG_WRITE_SCORES, scores=scores)
+    assert int(status.item()) == mla.MLA_DEV_INDEX_OUT_OF_RANGE
+    w.indices = clean
+    ref = oracle_ref(w, want_weights=True)
+    assert rel_err(o_lat, ref["o_lat"]) <= REL_TOL
+    assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
+    check_rowsums(ref, lse, None, bf16_query_scores(ref, w.q_pe, slot_rows(w), w.scale))
+    assert attended_sets_equal(bitmap, w)
+    # Two kernels' bf16 results from differently ordered fp32 sums: a rounding apart.
+    assert rel_err(f64(out), f64(out2)) <= 2 * 2.0 ** -8
+    assert np.max(np.abs(lse - f64(bufs2.lse))) <= 1e-4
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_decode_dense_ragged_stops_at_length(mla, S):
+    """Dense selection with ragged lengths: unless per-slot scores are
+    requested a split stops at L_b (splits past it are empty) and the result
+    matches the oracle."""
+    w = workload.make("dense_p1000_b1", B=3, L=1001)
+    w.seq_lens = torch.tensor([1001, 300, 37], dtype=torch.int32)
+    g = to_gpu(w)
+    bufs, out = _run_decode(mla, g, S)
+    ref = oracle_ref(w, want_weights=True)
+    assert rel_err(f64(bufs.o_latent), ref["o_lat"]) <= REL_TOL
+    assert rel_err(f64(out)[:, 0], ref["out"]) <= REL_TOL
+    check_rowsums(ref, f64(bufs.lse), None, bf16_query_scores(ref, w.q_pe, slot_rows(w), w.scale))
