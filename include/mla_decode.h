@@ -55,7 +55,7 @@ extern "C" {
 #define MLA_VALUE_DIM 128
 
 /* Most index slots one split may hold in sparse mode (indices != NULL). */
-#define MLA_MAX_SLOTS_PER_SPLIT 1024
+#define MLA_MAX_SLOTS_PER_SPLIT 2048
 #define MLA_MAX_SPLITS 64
 
 typedef enum {

@@ -23,7 +23,7 @@ MLA_DEV_INDEX_OUT_OF_RANGE = 1
 MLA_DEV_DUPLICATE_INDEX = 2
 MLA_DEV_EMPTY_SELECTION = 4
 HEADS, NOPE, ROPE, LATENT, VALUE = 128, 128, 64, 512, 128
-MAX_SLOTS_PER_SPLIT = 1024
+MAX_SLOTS_PER_SPLIT = 2048
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_mla_amd.build`")

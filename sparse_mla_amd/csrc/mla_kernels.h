@@ -13,7 +13,7 @@ constexpr int kRope = 64;
 constexpr int kLatent = 512;
 constexpr int kValue = 128;
 constexpr int kRowsPerHead = kNope + kValue;  // 256 rows of wkv_b per head
-constexpr int kIdxCap = 1024;                  // index slots staged per split
+constexpr int kIdxCap = 2048;                  // index slots staged per split
 
 // Block-scaled fp8 weight (read instead of wkv_b when w_fp8 != NULL): E4M3FN
 // codes [32768][512] and fp32 scales [256][4], one per 128 x 128 block.

@@ -775,8 +775,8 @@ constexpr int kOffQ = kBufBytes;
 constexpr int kQWave = 7 * kBlk * 128;
 constexpr int kOffIdx = kOffQ + 4 * kQWave;  // int [kIdxCap]
 constexpr int kOffLen = kOffIdx + kIdxCap * 4;  // int [4][64]: the sequence length, per wave
-constexpr int kOffTot = kOffLen + 4 * 64 * 4;   // int [4]: valid slots per wave (compaction)
-constexpr int kDecodeLds = kOffTot + 4 * 4;
+constexpr int kOffTot = kOffLen + 4 * 64 * 4;   // int [2][4]: valid slots per half and wave (compaction)
+constexpr int kDecodeLds = kOffTot + 8 * 4;
 constexpr int kSoftSteps = 32;              // softmax steps placed beside MFMAs
 static_assert(kDecodeLds <= 160 * 1024, "decode LDS budget");
 constexpr int kTilePitch = 1040;            // output tile row: 512 bf16 + 16 bytes of padding
@@ -887,7 +887,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   // Every load of the prologue is an LDS-DMA: query lines 7 and 8 (8 per
   // wave), the sequence length (lane 0 of each wave; the other lanes read
   // past the 4-byte range and land zeros), this split's index slots (slot i
-  // lands at sidx[i]; slots past nslot read as zeros and are masked below),
+  // lands at sidx[i], in groups of 256; slots past nslot are masked below),
   // then query lines 0 .. 6 (28 per wave).  With no
   // compiler-visible load the only waits are the explicit ones below (a
   // compiler-placed wait for an ordinary load would also drain the query
@@ -899,10 +899,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
        lds0 + (uint32_t)(kOffLen + 256 * wave), 4u * (uint32_t)lane);
   if constexpr (!dense) {
     // 4 bytes per lane, so that the range check (nslot slots) is per slot.
+    // Wave w moves the slots its own threads validate below (each wave waits
+    // for its own loads only): 256 w .. 256 w + 255, and with more than 1024
+    // slots also 1024 + 256 w .. 1024 + 256 w + 255.
     const i32x4 ri = buffer_rsrc(a.indices + (int64_t)b * a.k_max + s0, (uint32_t)nslot * 4u);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       dma4(ri, lds0 + (uint32_t)(kOffIdx + 4 * (256 * wave + 64 * k)), 4u * (uint32_t)(256 * wave + 64 * k + lane));
+    if (nslot > kIdxCap / 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        dma4(ri, lds0 + (uint32_t)(kOffIdx + 4 * (kIdxCap / 2 + 256 * wave + 64 * k)),
+             4u * (uint32_t)(kIdxCap / 2 + 256 * wave + 64 * k + lane));
+    }
   }
   stage_query(0, 7);
   asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
@@ -916,55 +925,75 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeArgs a) {
   const bool keep_slots = (a.flags & 2u) != 0;  // per-slot scores: slot order kept
   if constexpr (!dense) {
     {
-      const int i0 = 4 * tid;
-      const int4 raw = *reinterpret_cast<const int4*>(sidx + i0);
-      int r[4] = {raw.x, raw.y, raw.z, raw.w};
-      int cnt = 0;
+      // Thread tid: slots 4 tid .. 4 tid + 3 of each half (h = 0: slot
+      // 4 tid + e, h = 1: slot 1024 + 4 tid + e; past nslot: masked).
+      int r[2][4];
+      int cnt[2] = {0, 0};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = r[e];
-        const bool ok = (i0 + e < nslot) && t >= 0 && t < Lb;
-        if (validate && i0 + e < nslot) {
-          // Prefill: a key after the token (but inside the prompt) is
-          // removed by the causal mask, not an error.
-          if (!ok && t != -1 && !(causal && t >= Lb && t < a.max_len)) atomicOr(a.status, 1u);
-          if (ok) {
-            const uint32_t bit = 1u << (t & 31);
-            const uint32_t old = atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), bit);
-            if (old & bit) atomicOr(a.status, 2u);
+      for (int h = 0; h < 2; ++h) {
+        const int i0 = h * (kIdxCap / 2) + 4 * tid;
+        const int4 raw = *reinterpret_cast<const int4*>(sidx + i0);
+        const int v[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = v[e];
+          const bool ok = (i0 + e < nslot) && t >= 0 && t < Lb;
+          if (validate && i0 + e < nslot) {
+            // Prefill: a key after the token (but inside the prompt) is
+            // removed by the causal mask, not an error.
+            if (!ok && t != -1 && !(causal && t >= Lb && t < a.max_len)) atomicOr(a.status, 1u);
+            if (ok) {
+              const uint32_t bit = 1u << (t & 31);
+              const uint32_t old = atomicOr(a.bitmap + (int64_t)b * a.bitmap_words + (t >> 5), bit);
+              if (old & bit) atomicOr(a.status, 2u);
+            }
           }
+          r[h][e] = ok ? t : -1;
+          cnt[h] += ok ? 1 : 0;
         }
-        r[e] = ok ? t : -1;
-        cnt += ok ? 1 : 0;
       }
       if (keep_slots) {
-        *reinterpret_cast<int4*>(sidx + i0) = make_int4(r[0], r[1], r[2], r[3]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<int4*>(sidx + h * (kIdxCap / 2) + 4 * tid) = make_int4(r[h][0], r[h][1], r[h][2], r[h][3]);
       } else {
         // Stable compaction: the valid slots, in slot order, to the front.
-        // This thread's place = the valid slots of the threads before it:
-        // within the wave from the three bit planes of cnt (0 .. 4), across
-        // waves from the per-wave totals in LDS.
-        const uint64_t p0 = __builtin_amdgcn_ballot_w64((cnt & 1) != 0);
-        const uint64_t p1 = __builtin_amdgcn_ballot_w64((cnt & 2) != 0);
-        const uint64_t p2 = __builtin_amdgcn_ballot_w64((cnt & 4) != 0);
+        // A slot's place = the valid slots before it: in its half, those of
+        // the threads before this one (within the wave from the three bit
+        // planes of the count, 0 .. 4; across waves from per-wave totals in
+        // LDS), after all of the first half's for the second.
         auto below = [&](uint64_t m) __attribute__((always_inline)) {
           return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         };
-        const int before = below(p0) + 2 * below(p1) + 4 * below(p2);
-        int* stot = reinterpret_cast<int*>(smem + kOffTot);
-        if (lane == 0) stot[wave] = __popcll(p0) + 2 * __popcll(p1) + 4 * __popcll(p2);
-        __syncthreads();  // the totals are in; every thread holds its raw slots
-        int base = 0, total = 0;
+        int* stot = reinterpret_cast<int*>(smem + kOffTot);  // [half][wave]
+        int before[2];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int tw = stot[w];
-          base += w < wave ? tw : 0;
-          total += tw;
+        for (int h = 0; h < 2; ++h) {
+          const uint64_t p0 = __builtin_amdgcn_ballot_w64((cnt[h] & 1) != 0);
+          const uint64_t p1 = __builtin_amdgcn_ballot_w64((cnt[h] & 2) != 0);
+          const uint64_t p2 = __builtin_amdgcn_ballot_w64((cnt[h] & 4) != 0);
+          before[h] = below(p0) + 2 * below(p1) + 4 * below(p2);
+          if (lane == 0) stot[4 * h + wave] = __popcll(p0) + 2 * __popcll(p1) + 4 * __popcll(p2);
         }
-        int pos = base + before;
+        __syncthreads();  // the totals are in; every thread holds its raw slots
+        int base[2] = {0, 0}, total = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (r[e] >= 0) sidx[pos++] = r[e];
+        for (int h = 0; h < 2; ++h) {
+          base[h] = total;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int tw = stot[4 * h + w];
+            base[h] += w < wave ? tw : 0;
+            total += tw;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int pos = base[h] + before[h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r[h][e] >= 0) sidx[pos++] = r[h][e];
+        }
         // The last block's slots past the valid ones are masked.
         for (int i = total + tid; i < ((total + kBlk - 1) & ~(kBlk - 1)); i += 256) sidx[i] = -1;
         nkeys = total;

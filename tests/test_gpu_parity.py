@@ -93,6 +93,7 @@ CASES = [
     ("dense_p1000_b1", 3, 1001, None, 24, "split"),           # 3 rows, 24 splits (8 empty), two passes
     ("sparse_b32_l4096_k2048", 2, 4096, 2048, 64, "packed"),  # the most splits: one block each
     ("sparse_b32_l4096_k2048", 33, 300, 100, 2, "packed"),    # 32-row value-up tiles, a 1-row tile
+    ("sparse_b32_l4096_k2048", 2, 4096, 2048, 1, "packed"),   # one split of 2048 slots: the whole index region
 ]
 
 
@@ -213,8 +214,8 @@ def _split_chunk(k_max, S):
     return -(-c // 32) * 32
 
 
-@pytest.mark.parametrize("S", [1, 3])
-def test_decode_masked_slots_compacted(mla, S):
+@pytest.mark.parametrize("L,k,S", [(300, 200, 1), (300, 200, 3), (3000, 1900, 1)])
+def test_decode_masked_slots_compacted(mla, L, k, S):
     """Slots that select nothing (-1 padding, a negative value, values past
     the sequence) scattered through every row, and with several splits one
     split of a row holding none at all: unless per-slot scores are requested
@@ -223,7 +224,7 @@ def test_decode_masked_slots_compacted(mla, S):
     (invalid slots given to it as -1), the row sums hold, the attended bitmap
     and the out-of-range status are exact, and the result equals the
     slot-order path (per-slot scores requested) up to rounding."""
-    w = workload.make("sparse_b32_l4096_k2048", B=5, L=300, k=200)
+    w = workload.make("sparse_b32_l4096_k2048", B=5, L=L, k=k)
     gen = torch.Generator().manual_seed(41)
     idx = w.indices.clone()
     idx[torch.rand(idx.shape, generator=gen) < 0.5] = -1
@@ -231,9 +232,9 @@ def test_decode_masked_slots_compacted(mla, S):
     idx[past] = 100000                      # past every length: masked, flagged
     idx[0, 10] = -7                         # negative and not -1: masked, flagged
     if S > 1:
-        idx[2, :_split_chunk(200, S)] = -1   # split 0 of row 2 selects nothing
+        idx[2, :_split_chunk(k, S)] = -1     # split 0 of row 2 selects nothing
     clean = idx.clone()
-    clean[(clean < 0) | (clean >= 300)] = -1
+    clean[(clean < 0) | (clean >= L)] = -1
     w.indices = idx
     g = to_gpu(w)
     words = (w.max_len + 31) // 32
