@@ -115,6 +115,9 @@ int launch_absorb(const AbsorbArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, void* stream);
 int launch_combine(const CombineArgs& a, void* stream);
 int launch_value_up(const ValueUpArgs& a, void* stream);  // fused combine when o_latent == NULL
+// From this many merged rows on (o_latent given) the value-up streams tiles
+// through workgroups that form W_UV,h once.
+constexpr int kValueUpStreamMinRows = 512;
 int launch_dequant(const DequantArgs& a, void* stream);
 int launch_output_proj(const OutProjArgs& a, void* stream);
 int launch_output_proj_pack(const uint16_t* wo, uint16_t* packed, void* stream);

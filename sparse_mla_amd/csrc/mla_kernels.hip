@@ -723,6 +723,104 @@ __global__ __launch_bounds__(256, 1) void value_up_kernel(const ValueUpArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// value-up of merged rows at large batches (o_latent given, e.g. the prefill's
+// B * T rows): workgroup = (head, slice of the batch's 32-row tiles), the
+// slices of a head on one XCD.  W_UV,h is formed in registers once per
+// workgroup (value_up_kernel forms it once per tile, so at thousands of rows
+// every tile re-read it); the slice's tiles stream through four LDS buffers,
+// wave w moving rows 8 w .. 8 w + 7 of each (one 1 KB row per LDS-DMA
+// instruction, rows past B masked), three tiles ahead, one barrier per tile.
+// Each tile is multiplied exactly as in value_up_kernel (same operands, same
+// order): the results are identical.
+// ---------------------------------------------------------------------------
+constexpr int kVsNbuf = 4;
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void value_up_stream_kernel(const ValueUpArgs a, int groups) {
+  __shared__ __attribute__((aligned(1024))) char tiles[kVsNbuf * 32 * kOtRow];
+  const int units = a.H * groups;
+  const int per_xcd = (units + 7) >> 3;
+  const int unit = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (unit >= units) return;
+  const int h = unit / groups, g = unit % groups;
+  const int ntiles = (a.B + 31) / 32;
+  const int t0 = (int)((int64_t)ntiles * g / groups), t1 = (int)((int64_t)ntiles * (g + 1) / groups);
+  if (t0 >= t1) return;
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(char LDS_AS*)tiles;
+  const uint32_t row_bytes = (uint32_t)a.H * kLatent * 2u;  // between consecutive batch rows of one head
+
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t buf = lds0 + (uint32_t)((t % kVsNbuf) * 32 * kOtRow);
+    const int nv = t < t1 ? min(32, a.B - 32 * t) : 0;  // rows of the tile that exist (none past the slice)
+    const i32x4 rs = buffer_rsrc(a.o_latent + ((int64_t)(t < t1 ? 32 * t : 0) * a.H + h) * kLatent,
+                                 nv > 0 ? (uint32_t)(nv - 1) * row_bytes + 1024u : 0u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t r = (uint32_t)(8 * wave + j);
+      dma16(rs, buf + r * (uint32_t)kOtRow, r * row_bytes + 16u * (uint32_t)lane);
+    }
+  };
+  issue(t0);
+  issue(t0 + 1);
+  issue(t0 + 2);
+
+  // W_UV,h rows 32 w + l % 32, columns 16 st + 8 (l / 32) .. + 7, as in
+  // value_up_kernel.  Pinned before the loop: the compiler's wait for these
+  // loads (which also covers the three tiles issued before them) sits here,
+  // and none inside the loop drains the tiles in flight.
+  const size_t wrow = ((size_t)h * kRowsPerHead + kNope + 32 * wave + (lane & 31)) * kLatent + 8 * hh;
+  bf16x8 wf[32];
+  if constexpr (FP8) {
+    uint2 wr[32];
+#pragma unroll
+    for (int st = 0; st < 32; ++st) wr[st] = *reinterpret_cast<const uint2*>(a.fp8.w_fp8 + wrow + 16 * st);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sc = a.fp8.w_scale[(2 * h + 1) * (kLatent / 128) + j];
+      if (__builtin_expect(block_has_ties(sc, lane), 0)) {
+#pragma unroll
+        for (int st = 8 * j; st < 8 * j + 8; ++st) wf[st] = dq8<true>(wr[st], sc);
+      } else {
+#pragma unroll
+        for (int st = 8 * j; st < 8 * j + 8; ++st) wf[st] = dq8<false>(wr[st], sc);
+      }
+    }
+    if (a.fp8.w_formed != nullptr && t0 == 0) {
+#pragma unroll
+      for (int st = 0; st < 32; ++st) *reinterpret_cast<bf16x8*>(a.fp8.w_formed + wrow + 16 * st) = wf[st];
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < 32; ++st) wf[st] = ld8(a.wkv_b + wrow + 16 * st);
+  }
+#pragma unroll
+  for (int st = 0; st < 32; ++st) asm volatile("" : "+v"(wf[st]));
+
+  for (int t = t0; t < t1; ++t) {
+    // This wave's rows of tile t are in when only tiles t + 1 and t + 2 (16
+    // loads) are outstanding; the barrier makes the tile every wave's and
+    // frees buffer (t + 3) % 4, read in the previous iteration.
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    __syncthreads();
+    issue(t + 3);
+    f32x16 acc = {};
+    const char LDS_AS* ol = (const char LDS_AS*)tiles + (t % kVsNbuf) * 32 * kOtRow + (lane & 31) * kOtRow + 16 * hh;
+#pragma unroll
+    for (int st = 0; st < 32; ++st) acc = mfma32(wf[st], *(const bf16x8 LDS_AS*)(ol + 32 * st), acc);
+    const int b = 32 * t + (lane & 31);
+    if (b < a.B) {
+      uint16_t* out = a.out + (int64_t)b * a.out_sb + (int64_t)h * a.out_sh + 32 * wave + 4 * hh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<uint2*>(out + 8 * q4) = pack4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    }
+  }
+  // The masked loads issued past the slice may still be landing.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // decode: sparse flash-decode over the selected cache rows.
 //
 // Workgroup = (sequence b, key split s), all 128 heads, 4 waves, one
@@ -1661,6 +1759,18 @@ static void launch_value_up_t(const ValueUpArgs& a, dim3 grid, bool small, bool 
 }
 
 int launch_value_up(const ValueUpArgs& a, void* stream) {
+  if (a.o_latent != nullptr && a.B >= kValueUpStreamMinRows) {
+    // Merged rows at large batches: W_UV,h formed once per workgroup, the
+    // tiles streamed; enough workgroups per head to give every CU one.
+    const int ntiles = (a.B + 31) / 32;
+    const int groups = max(1, min(ntiles, (256 + a.H - 1) / a.H));
+    const int units = a.H * groups;
+    const dim3 grid(8 * ((units + 7) / 8));
+    const hipStream_t st = (hipStream_t)stream;
+    if (a.fp8.w_fp8 != nullptr) hipLaunchKernelGGL(value_up_stream_kernel<true>, grid, dim3(256), 0, st, a, groups);
+    else hipLaunchKernelGGL(value_up_stream_kernel<false>, grid, dim3(256), 0, st, a, groups);
+    return (int)hipGetLastError();
+  }
   // 32-row tiles, or 16 when that is what it takes to give every CU a tile.
   // Two splits staged per pass when there are at most two (half the LDS, so
   // two workgroups fit a CU), else four.
