@@ -1,4 +1,4 @@
-// Sanitizer driver for the host side of libmla_decode
+// Sanitizer check program for the host side of libmla_decode
 // (sparse_mla_amd/csrc/mla_api.cpp): built by tests/test_sanitizers.py with
 // AddressSanitizer and UndefinedBehaviorSanitizer against stub launchers that
 // record the kernel arguments instead of launching (no GPU, no HIP).  It
@@ -117,6 +117,6 @@ int main() {
   CHECK(mla_output_proj_pack(P(F), P(F + 16), nullptr) == MLA_OK);
   CHECK(mla_output_proj_pack(P(F), P(F + 2), nullptr) == MLA_ERR_ALIGNMENT);
   for (int code = 0; code <= 8; ++code) CHECK(mla_status_string(code) != nullptr);
-  puts("api sanitizer driver: ok");
+  puts("api sanitizer check: ok");
   return 0;
 }

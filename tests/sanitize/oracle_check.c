@@ -1,5 +1,5 @@
 /*
- * Sanitizer driver for the C oracle (oracle/mla_oracle.c), built by
+ * Sanitizer check program for the C oracle (oracle/mla_oracle.c), built by
  * tests/test_sanitizers.py with AddressSanitizer and UndefinedBehaviorSanitizer
  * and linked against the oracle's source.  Every array is allocated at its
  * exact size, so an access one element past any of them is reported.  It
@@ -34,7 +34,7 @@ static double rnd(void) {
     state = state * 6364136223846793005ULL + 1442695040888963407ULL;
     return ((double)(state >> 11) / 9007199254740992.0) * 2.0 - 1.0;
 }
-/* Every block this driver allocates, freed at the end so that leak
+/* Every block this program allocates, freed at the end so that leak
  * detection reports only the oracle's own allocations. */
 static void* blocks[64];
 static int nblocks = 0;
@@ -110,6 +110,6 @@ int main(void) {
     double* ex = (double*)take(sizeof(double) * (size_t)(R * C));
     CHECK(oracle_dequant_fp8(codes, scl, R, C, BLK, b16, ex) == 0);
     for (int i = 0; i < nblocks; ++i) free(blocks[i]);
-    puts("oracle sanitizer driver: ok");
+    puts("oracle sanitizer check: ok");
     return 0;
 }

@@ -1,12 +1,12 @@
 """AddressSanitizer / UndefinedBehaviorSanitizer builds of the host code.
 
-Two drivers under ``tests/sanitize/`` are compiled with
+Two check programs under ``tests/sanitize/`` are compiled with
 ``-fsanitize=address,undefined -fno-sanitize-recover=all`` and run:
 
-* ``oracle_driver.c`` links ``oracle/mla_oracle.c`` and calls every oracle
+* ``oracle_check.c`` links ``oracle/mla_oracle.c`` and calls every oracle
   function on small ragged inputs, including the padding, repeat, empty-row
   and out-of-range paths (leak checking on).
-* ``api_driver.cpp`` links ``sparse_mla_amd/csrc/mla_api.cpp`` -- the host
+* ``api_check.cpp`` links ``sparse_mla_amd/csrc/mla_api.cpp`` -- the host
   argument checks, plans and workspace layouts of every C-ABI entry point --
   against stub launchers that record the kernel arguments instead of
   launching, and drives it with valid, invalid and extreme arguments.
@@ -38,13 +38,13 @@ def _build_and_run(cmd, exe, expect):
 
 
 def test_oracle_under_sanitizers(tmp_path):
-    exe = tmp_path / "oracle_driver"
-    _build_and_run(["gcc", *SAN, "-fopenmp", "tests/sanitize/oracle_driver.c", "oracle/mla_oracle.c",
-                    "-lm", "-o", str(exe)], exe, "oracle sanitizer driver: ok")
+    exe = tmp_path / "oracle_check"
+    _build_and_run(["gcc", *SAN, "-fopenmp", "tests/sanitize/oracle_check.c", "oracle/mla_oracle.c",
+                    "-lm", "-o", str(exe)], exe, "oracle sanitizer check: ok")
 
 
 def test_api_host_checks_under_sanitizers(tmp_path):
-    exe = tmp_path / "api_driver"
+    exe = tmp_path / "api_check"
     _build_and_run(["g++", "-std=c++17", *SAN, "-Iinclude", "-Isparse_mla_amd/csrc",
-                    "tests/sanitize/api_driver.cpp", "sparse_mla_amd/csrc/mla_api.cpp", "-o", str(exe)],
-                   exe, "api sanitizer driver: ok")
+                    "tests/sanitize/api_check.cpp", "sparse_mla_amd/csrc/mla_api.cpp", "-o", str(exe)],
+                   exe, "api sanitizer check: ok")
