@@ -365,8 +365,10 @@ int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int6
  * fp8 dequantisation).  mla_output_proj reads, per chunk of 256 inputs, a
  * 512-byte piece of each of 7168 weight rows 32 KB apart; the packed layout
  * stores each group of 28 output rows chunk by chunk, so the same bytes are
- * read as one contiguous stream per group (measured about 10 % faster at batches
- * up to 32; no change at 64, where reading x sets the pace).
+ * read as one contiguous stream per group.  Since the workgroups of
+ * mla_output_proj start their walk over the inputs at different chunks, the
+ * two reach about the same rate at every batch (measured within a few
+ * percent either way).
  *   mla_output_proj_pack: wo_packed[g][c][r][k] = wo[28 g + r][256 c + k]
  *     for g < 256, c < 64, r < 28, k < 256; wo and wo_packed bf16, 7168 x 16384
  *     elements each (235 MB), 16-byte aligned, not overlapping.

@@ -1563,6 +1563,7 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
   constexpr int kWaveLds = 3 * kSegs * 128;      // three buffers per wave
   constexpr int kDpc = 4 + XR / 8;               // DMA instructions per wave per chunk
   constexpr int kChunks = kWoIn / kOpChunk;      // 64
+  static_assert((kChunks & (kChunks - 1)) == 0, "the chunk walk wraps with a mask");
   __shared__ __attribute__((aligned(1024))) char smem[4 * kWaveLds];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1572,10 +1573,18 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
   const i32x4 rw = buffer_rsrc(a.wo + (size_t)o0 * kWoIn, (uint32_t)(kOpRows * kWoIn * 2));
   const i32x4 rx = buffer_rsrc(a.x, (uint32_t)(((int64_t)(a.B - 1) * a.x_sb + kWoIn) * 2));
   const uint32_t r8 = (uint32_t)(lane >> 3);
-  // Chunk c into buffer c % 3: instruction j moves rows 8j .. 8j + 7 (lane l:
-  // row 8j + l / 8, position l % 8, source chunk (l % 8) ^ seg_swz(row)).
-  auto issue = [&](int c) __attribute__((always_inline)) {
-    const uint32_t buf = lds_w + (uint32_t)((c % 3) * kSegs * 128);
+  // Workgroup x walks K from chunk x / 8 on (wrapping round): were every
+  // workgroup at the same chunk, the plain layout's weight reads (pieces of
+  // rows 32 KB apart, all at one column offset) would crowd into the same
+  // memory channels; staggered, it reads as fast as the packed layout.  The
+  // packed layout takes the same order, so the two give identical sums.
+  const int c_first = (int)blockIdx.x >> 3;
+  // Step it's chunk c = (c_first + it) mod 64 into buffer it % 3: instruction j
+  // moves rows 8j .. 8j + 7 (lane l: row 8j + l / 8, position l % 8, source
+  // chunk (l % 8) ^ seg_swz(row)).
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const uint32_t buf = lds_w + (uint32_t)((it % 3) * kSegs * 128);
+    const int c = (c_first + it) & (kChunks - 1);
     const uint32_t col = (uint32_t)(c * kOpChunk + 64 * wave) * 2u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1608,14 +1617,14 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
   for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
   issue(0);
   issue(1);
-  for (int c = 0; c < kChunks; ++c) {
-    // Chunk c has landed when at most chunk c + 1's loads are outstanding.
-    if (c + 1 < kChunks) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDpc) : "memory");
+  for (int it = 0; it < kChunks; ++it) {
+    // Step it's chunk has landed when at most step it + 1's loads are outstanding.
+    if (it + 1 < kChunks) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDpc) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // Buffer (c + 2) % 3 last held chunk c - 1, whose fragments were read
-    // (and used) in the previous iteration.
-    if (c + 2 < kChunks) issue(c + 2);
-    const char LDS_AS* buf = wl + (c % 3) * kSegs * 128;
+    // Buffer (it + 2) % 3 last held step it - 1's chunk, whose fragments were
+    // read (and used) in the previous iteration.
+    if (it + 2 < kChunks) issue(it + 2);
+    const char LDS_AS* buf = wl + (it % 3) * kSegs * 128;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bf16x8 af = frag(buf, 0u, t);
