@@ -236,11 +236,14 @@ __device__ __forceinline__ bool block_has_ties(float s, int lane) {
 // at a time, laid out like a gathered block of the decode (row r of a tile,
 // line m = d / 64 at m * 4 KB + r * 128, chunk swizzled by seg_swz(r)), so
 // each load moves whole lines; read directly, each would touch 32 rows for
-// 32 bytes apiece.  With no compiler-visible load, every wait is explicit.
+// 32 bytes apiece.  Two sets of four tiles alternate: with more than 128
+// batch rows the next group's tiles arrive while the current group's
+// products and stores run.  With no compiler-visible load, every wait is
+// explicit.
 // ---------------------------------------------------------------------------
 constexpr int kAbsQ = 32 * 1024;             // one quarter of the slab
 constexpr int kAbsQTile = 2 * 32 * 128;      // one 32-row query tile (8 KB)
-constexpr int kAbsLds = 2 * kAbsQ + 4 * kAbsQTile;
+constexpr int kAbsLds = 2 * kAbsQ + 8 * kAbsQTile;
 
 // With FP8 the slab is read as block-scaled fp8 codes (32 KB per half, one
 // scale per quarter: its 128 rows and 128 columns are one scale block) by
@@ -322,10 +325,11 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
     }
   };
   uint4 raw0[4], raw1[4];
-  // Query tiles bt0 .. bt0 + 3 (those that exist): 8 instructions per tile,
-  // 2 per wave; rows past B load row B - 1 (their columns are never stored).
+  // Query tiles bt0 .. bt0 + 3 (those that exist) into tile set `set`: 8
+  // instructions per tile, 2 per wave; rows past B load row B - 1 (their
+  // columns are never stored).
   const int nbt = (a.B + 31) / 32;
-  auto stage_q = [&](int bt0) __attribute__((always_inline)) {
+  auto stage_q = [&](int bt0, int set) __attribute__((always_inline)) {
     const i32x4 rq = buffer_rsrc(a.q_nope + (int64_t)h * a.q_sh, (uint32_t)(((int64_t)(a.B - 1) * a.q_sb + kNope) * 2));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
         const uint32_t r = (uint32_t)(8 * g + (lane >> 3));
         const int bb = min((bt0 + u) * 32 + (int)r, a.B - 1);
         const uint32_t c16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
-        dma16(rq, qt0 + (uint32_t)(u * kAbsQTile + m * 32 * 128 + 8 * g * 128),
+        dma16(rq, qt0 + (uint32_t)((4 * set + u) * kAbsQTile + m * 32 * 128 + 8 * g * 128),
               (uint32_t)((int64_t)bb * a.q_sb * 2) + (uint32_t)(m * 128) + c16);
       }
     }
@@ -398,26 +402,24 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
   bf16x8 qb[4][8];
   for (int bt0 = 0; bt0 < nbt; bt0 += 4) {
     const int nq = min(4, nbt - bt0);
+    const int set = (bt0 >> 2) & 1;
     if (bt0 == 0) {
       // Quarter 0 of the slab, the first query tiles, quarter 1 of the slab.
       if constexpr (FP8) {
         load_slab8(0, raw0);
-        stage_q(0);
+        stage_q(0, 0);
         load_slab8(1, raw1);
         store_slab8(0, raw0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
         stage_slab(0);
-        stage_q(0);
+        stage_q(0, 0);
         stage_slab(1);
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       }
     } else {
-      // Every wave is done with the previous query tiles (their reads
-      // completed before its last copy-out, which precedes the barrier of
-      // its last output tile).
-      __syncthreads();
-      stage_q(bt0);
+      // This group's tiles were requested during the previous group: after
+      // this wait this wave's have landed, after the barrier every wave's.
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
@@ -426,8 +428,15 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
     for (int u = 0; u < 4; ++u) {
       if (u >= nq) break;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) qb[u][st] = *(const bf16x8 LDS_AS*)(wl + (qt0 - lds0) + u * kAbsQTile + qk_off(st));
+      for (int st = 0; st < 8; ++st)
+        qb[u][st] = *(const bf16x8 LDS_AS*)(wl + (qt0 - lds0) + (4 * set + u) * kAbsQTile + qk_off(st));
     }
+    // The next group's tiles go into the other set, which held the group
+    // before this one: every wave read those into registers before the
+    // barriers of that group's output tiles, which precede the barrier
+    // above.  (The first group requests them only after quarter 1 of the
+    // slab has landed, whose wait would otherwise also wait for them.)
+    if (bt0 > 0 && bt0 + 4 < nbt) stage_q(bt0 + 4, set ^ 1);
     if (bt0 == 0) {
       // The quarter-0 region holds output tiles from here on.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -443,6 +452,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const AbsorbArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       read_slab(1, af1);
+      if (4 < nbt) stage_q(4, 1);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
