@@ -109,6 +109,10 @@ def test_fp8_calls_equal_bf16_calls(mla):
     B = 45
     q = torch.randn((B, 1, 128, 128), generator=g).to(torch.bfloat16).to(dev)
     assert torch.equal(mla.mla_absorb_q_fp8(q, c, s), mla.mla_absorb_q(q, wbf))
+    # 300 rows: ten 32-row query tiles in three groups, the later ones
+    # staged while the one before is computed, in both tile sets.
+    q3 = torch.randn((300, 1, 128, 128), generator=g).to(torch.bfloat16).to(dev)
+    assert torch.equal(mla.mla_absorb_q_fp8(q3, c, s), mla.mla_absorb_q(q3, wbf))
     o = torch.randn((B, 128, 512), generator=g).to(torch.bfloat16).to(dev)
     assert torch.equal(mla.mla_value_up_fp8(o, c, s), mla.mla_value_up(o, wbf))
     for S in (2, 4):

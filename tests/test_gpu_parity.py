@@ -30,11 +30,13 @@ def test_absorb_q(mla):
     assert rel_err(f64(q_abs), ref) <= 4e-3
 
 
-def test_absorb_q_many_batch_tiles(mla):
-    """B = 200: seven 32-row batch tiles, so the query rows are staged in two
-    groups of at most four tiles (the second after the first group's tiles
-    are written)."""
-    w = workload.make("sparse_b32_l4096_k2048", B=200, L=8, k=4)
+@pytest.mark.parametrize("B", [200, 300])
+def test_absorb_q_many_batch_tiles(mla, B):
+    """More than four 32-row batch tiles: the query rows are staged in groups
+    of at most four tiles, each group's tiles requested while the group
+    before it is computed, into two alternating tile sets (B = 200: groups
+    of 4 and 3; B = 300: 4, 4 and 2, the third reusing the first set)."""
+    w = workload.make("sparse_b32_l4096_k2048", B=B, L=8, k=4)
     g = to_gpu(w)
     q_abs = mla.mla_absorb_q(g.q_nope, g.wkv_b)
     torch.cuda.synchronize()
