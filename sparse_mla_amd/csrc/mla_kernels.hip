@@ -808,9 +808,12 @@ __global__ __launch_bounds__(256, 1) void value_up_stream_kernel(const ValueUpAr
   for (int st = 0; st < 32; ++st) asm volatile("" : "+v"(wf[st]));
 
   for (int t = t0; t < t1; ++t) {
-    // This wave's rows of tile t are in when only tiles t + 1 and t + 2 (16
-    // loads) are outstanding; the barrier makes the tile every wave's and
-    // frees buffer (t + 3) % 4, read in the previous iteration.
+    // This wave's rows of tile t are in when at most 16 of its memory
+    // operations are outstanding: tiles t + 1 and t + 2 are 16 loads, and
+    // the output stores of the iterations since also count, so the wait is
+    // conservative (it can cover part of tile t + 1, never end early).  The
+    // barrier makes the tile every wave's and frees buffer (t + 3) % 4, read
+    // in the previous iteration.
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     __syncthreads();
     issue(t + 3);
