@@ -387,9 +387,23 @@ def main():
         oproj["packed_weights"] = {"us": pk_ms * 1e3, "achieved_GBps": op_bytes / (pk_ms * 1e-3) / 1e9,
                                    "frac_hbm": op_bytes / (pk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                    "kernel": "mla_output_proj_packed (weight from mla_output_proj_pack)"}
+        # The inputs split in four (mla_output_proj_split: fp32 partial sums
+        # in a workspace, added by a second launch), on the plain weights.
+        ows = torch.empty(mla.mla_output_proj_split_workspace_bytes(B), dtype=torch.uint8, device="cuda")
+        for i in range(6):
+            mla.mla_output_proj_split(ox, wos[i % 3], ows, oout)
+        d0.record(stream)
+        for i in range(args.steps):
+            mla.mla_output_proj_split(ox, wos[i % 3], ows, oout)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        sp_ms = d0.elapsed_time(d1) / args.steps
+        oproj["split_inputs"] = {"us": sp_ms * 1e3, "achieved_GBps": op_bytes / (sp_ms * 1e-3) / 1e9,
+                                 "frac_hbm": op_bytes / (sp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "kernel": "mla_output_proj_split (4 input quarters, then their sum)"}
         log(f"output projection: {op_ms * 1e3:.2f} us ({oproj['achieved_GBps']:.0f} GB/s); "
-            f"packed weight {pk_ms * 1e3:.2f} us")
-        del ox, wos, wps, oout
+            f"packed weight {pk_ms * 1e3:.2f} us; inputs split in four {sp_ms * 1e3:.2f} us")
+        del ox, wos, wps, oout, ows
     # fp8 weights: the same rotated steps with absorb and value-up reading the
     # block-scaled fp8 weight directly (16.8 MB of codes per step instead of
     # the 33.5 MB bf16 copy the step above reads), five trials, median.

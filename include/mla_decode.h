@@ -380,6 +380,30 @@ int mla_output_proj_pack(const void* wo, void* wo_packed, void* stream);
 int mla_output_proj_packed(const void* x, int64_t x_sb, const void* wo_packed, void* out, int64_t out_sb,
                            int32_t B, void* stream);
 
+/*
+ * The output projection with its inputs split in four (the same "Attention
+ * update" passage and result up to fp32 rounding order): each quarter of
+ * i = 0 .. 16383 is summed by its own workgroups into an fp32 partial, and a
+ * second launch adds the four partials in quarter order and rounds to bf16
+ * once.  Each CU then reads a quarter of x instead of all of it, which is
+ * what limits mla_output_proj at large batches (measured faster from about
+ * 32 rows on; no faster below).
+ *   x, wo, out, x_sb, out_sb, B: as mla_output_proj.
+ *   workspace  device memory of at least mla_output_proj_split_workspace_bytes(B)
+ *              bytes (4 x min(B, 64) x 7168 fp32 partial sums), 16-byte aligned,
+ *              owned by the caller; its contents on entry do not matter, and it
+ *              must not be in use by another call until this one's launches
+ *              have completed on `stream`.
+ * Launches two kernels per 64 rows of the batch.  Errors: those of
+ * mla_output_proj, MLA_ERR_NULL_POINTER for a NULL workspace, MLA_ERR_ALIGNMENT
+ * for a misaligned one, MLA_ERR_WORKSPACE_TOO_SMALL.
+ * mla_output_proj_split_workspace_bytes: pure host function; 0 for B outside
+ * 1 .. 65536.
+ */
+size_t mla_output_proj_split_workspace_bytes(int32_t B);
+int mla_output_proj_split(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,8 @@ _combine_value_up_fp8 = _sig("mla_combine_value_up_fp8", ctypes.c_int,
 _output_proj = _sig("mla_output_proj", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p])
 _output_proj_pack = _sig("mla_output_proj_pack", ctypes.c_int, [_p, _p, _p])
 _output_proj_packed = _sig("mla_output_proj_packed", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p])
+_output_proj_split_ws = _sig("mla_output_proj_split_workspace_bytes", _sz, [_i32])
+_output_proj_split = _sig("mla_output_proj_split", ctypes.c_int, [_p, _i64, _p, _p, _i64, _i32, _p, _sz, _p])
 MODEL_DIM = 7168
 
 
@@ -426,6 +428,25 @@ def mla_output_proj_packed(x: torch.Tensor, wo_packed: torch.Tensor, out: Option
     B, x_sb, out, out_sb = _output_proj_args(x, wo_packed, out)
     _check("mla_output_proj_packed", _output_proj_packed(_ptr(x), x_sb, _ptr(wo_packed), _ptr(out), out_sb, B,
                                                          _stream(stream)))
+    return out
+
+
+def mla_output_proj_split_workspace_bytes(B: int) -> int:
+    return int(_output_proj_split_ws(B))
+
+
+def mla_output_proj_split(x: torch.Tensor, wo: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """mla_output_proj with the inputs split in four (fp32 partial sums in
+    `workspace`, a uint8 tensor of at least mla_output_proj_split_workspace_bytes(B)
+    bytes, allocated here when not given); same arguments and result up to
+    the rounding order of the fp32 sums."""
+    B, x_sb, out, out_sb = _output_proj_args(x, wo, out)
+    if workspace is None:
+        workspace = torch.empty(mla_output_proj_split_workspace_bytes(B), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check("mla_output_proj_split", _output_proj_split(_ptr(x), x_sb, _ptr(wo), _ptr(out), out_sb, B,
+                                                       _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -519,6 +519,7 @@ static int output_proj_impl(const void* x, int64_t x_sb, const void* wo, bool pa
     a.out_sb = out_sb;
     a.B = B - b0 < 64 ? B - b0 : 64;
     a.packed = packed;
+    a.part = nullptr;
     const int st = hip_status(mla::launch_output_proj(a, stream));
     if (st != MLA_OK) return st;
   }
@@ -528,6 +529,37 @@ static int output_proj_impl(const void* x, int64_t x_sb, const void* wo, bool pa
 int mla_output_proj(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
                     void* stream) {
   return output_proj_impl(x, x_sb, wo, false, out, out_sb, B, stream);
+}
+
+size_t mla_output_proj_split_workspace_bytes(int32_t B) {
+  if (B < 1 || B > 65536) return 0;
+  const int64_t rows = B < 64 ? B : 64;  // one launch's rows; larger batches reuse it launch after launch
+  return (size_t)(mla::kOpSplit * rows * mla::kWoOut) * sizeof(float);
+}
+
+int mla_output_proj_split(const void* x, int64_t x_sb, const void* wo, void* out, int64_t out_sb, int32_t B,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !wo || !out || !workspace) return MLA_ERR_NULL_POINTER;
+  if (B < 1 || B > 65536 || x_sb < mla::kWoIn || out_sb < mla::kWoOut) return MLA_ERR_BAD_DIM;
+  if (!aligned16(x) || !aligned16(wo) || !stride8(x_sb) || (reinterpret_cast<uintptr_t>(out) & 1u) != 0 ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGNMENT;
+  if (ws_bytes < mla_output_proj_split_workspace_bytes(B)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if ((63 * x_sb + mla::kWoIn) * 2 > (int64_t)UINT32_MAX) return MLA_ERR_RANGE;
+  for (int32_t b0 = 0; b0 < B; b0 += 64) {
+    mla::OutProjArgs a;
+    a.x = static_cast<const uint16_t*>(x) + (int64_t)b0 * x_sb;
+    a.wo = static_cast<const uint16_t*>(wo);
+    a.out = static_cast<uint16_t*>(out) + (int64_t)b0 * out_sb;
+    a.x_sb = x_sb;
+    a.out_sb = out_sb;
+    a.B = B - b0 < 64 ? B - b0 : 64;
+    a.packed = false;
+    a.part = static_cast<float*>(workspace);
+    const int st = hip_status(mla::launch_output_proj_split(a, stream));
+    if (st != MLA_OK) return st;
+  }
+  return MLA_OK;
 }
 
 int mla_output_proj_pack(const void* wo, void* wo_packed, void* stream) {

@@ -108,7 +108,11 @@ struct OutProjArgs {
   int64_t x_sb, out_sb;
   int32_t B;            // 1 .. 64
   bool packed;          // wo in the layout written by launch_output_proj_pack
+  float* part;          // launch_output_proj_split: [kOpSplit][B][kWoOut] fp32 partial sums
 };
+// K-split output projection: workgroup = 4 x 28 outputs over a quarter of
+// the inputs, the quarters' fp32 partial sums added by a second launch.
+constexpr int kOpSplit = 4;
 
 // Each returns a hipError_t value (0 on success).
 int launch_absorb(const AbsorbArgs& a, void* stream);
@@ -121,6 +125,7 @@ constexpr int kValueUpStreamMinRows = 512;
 int launch_dequant(const DequantArgs& a, void* stream);
 int launch_output_proj(const OutProjArgs& a, void* stream);
 int launch_output_proj_pack(const uint16_t* wo, uint16_t* packed, void* stream);
+int launch_output_proj_split(const OutProjArgs& a, void* stream);
 int device_cu_count(int* cus);
 
 // Static device scratch of mla_sparse_decode_noalloc: kScratchBytes per GPU.

@@ -1669,6 +1669,139 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
 }
 
 // ---------------------------------------------------------------------------
+// Output projection split over the inputs (mla_output_proj_split): each CU
+// of output_proj_kernel ingests all of x (2 MB at B = 64, twice its 0.9 MB of
+// wo), and at large batches that sets the rate.  Here workgroup (g, q) takes
+// 112 outputs (four 28-row tiles, tile w for wave w) over input quarter q
+// (4096 inputs), so a CU ingests a quarter of x beside the same 0.9 MB of wo;
+// the four quarters' fp32 partial sums go to a workspace and
+// output_proj_reduce_kernel adds them in quarter order.  K is walked in
+// chunks of 128 (two 128-byte lines per row): per chunk, wave w moves its
+// tile's 32 weight rows (rows past 28 masked) and a quarter of the x lines by
+// whole-line LDS-DMA into one of three buffers, two chunks ahead; the x lines
+// are shared by the four waves, so each chunk ends with a barrier.  Units are
+// numbered XCD-major (the quarters of a group share an XCD's L2 for x), and
+// the workgroups of XCD x start their walk at chunk 4 x (wrapping round), so
+// that the eight XCDs read different columns of wo at any moment while the
+// workgroups of one XCD read x's lines together.  Line l of row r at
+// segment l * R + r of its region (R = 32 rows per wo tile, 32 NT x rows),
+// 16-byte chunk c at position c ^ seg_swz(r).  M = o, N = b, K = i.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256, 1) void output_proj_split_kernel(const OutProjArgs a) {
+  constexpr int XR = 32 * NT;                    // x rows staged per chunk
+  constexpr int kQK = kWoIn / kOpSplit;          // 4096 inputs per quarter
+  constexpr int kNch = kQK / 128;                // 32 chunks
+  constexpr int kWoSegs = 4 * 64;                // four tiles x 2 lines x 32 rows
+  constexpr int kBufSegs = kWoSegs + 2 * XR;     // + 2 lines x XR rows of x
+  constexpr int kDpc = 8 + XR / 16;              // DMA instructions per wave per chunk
+  static_assert((kNch & (kNch - 1)) == 0, "the chunk walk wraps with a mask");
+  __shared__ __attribute__((aligned(1024))) char smem[3 * kBufSegs * 128];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int x8 = (int)blockIdx.x;
+  const int u = (x8 & 7) * 32 + (x8 >> 3);       // XCD-major unit
+  const int g = u >> 2, q = u & 3;               // output group, input quarter
+  const int o0 = 4 * kOpRows * g + kOpRows * wave;  // this wave's tile
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(char LDS_AS*)smem;
+  const i32x4 rw = buffer_rsrc(a.wo + (size_t)o0 * kWoIn + (size_t)q * kQK,
+                               (uint32_t)(((kOpRows - 1) * kWoIn + kQK) * 2));
+  const i32x4 rx = buffer_rsrc(a.x + (size_t)q * kQK, (uint32_t)(((int64_t)(a.B - 1) * a.x_sb + kQK) * 2));
+  const int c_first = (x8 & 7) * 4;
+  // Step it's chunk c into buffer it % 3.  Weight: instruction j moves lines
+  // 8j .. 8j + 7 of the tile (line li: row li % 32, half li / 32; lane l takes
+  // line 8j + l / 8, position l % 8).  x: wave w moves lines XR/2 w .. of the
+  // 2 XR (line li: row li % XR, half li / XR).
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const int c = (c_first + it) & (kNch - 1);
+    const uint32_t buf = lds0 + (uint32_t)((it % 3) * kBufSegs * 128);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t li = (uint32_t)(8 * j) + (uint32_t)(lane >> 3);
+      const uint32_t r = li & 31u, l = li >> 5;
+      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(r)) * 16u;
+      dma16(rw, buf + (uint32_t)(wave * 64 + 8 * j) * 128u,
+            r * (uint32_t)(kWoIn * 2) + (uint32_t)(c * 256) + l * 128u + q16);
+    }
+#pragma unroll
+    for (int j = 0; j < XR / 16; ++j) {
+      const uint32_t li = (uint32_t)(wave * (XR / 2) + 8 * j) + (uint32_t)(lane >> 3);
+      const uint32_t b = li & (uint32_t)(XR - 1), l = li / (uint32_t)XR;
+      const uint32_t q16 = (((uint32_t)(lane & 7)) ^ seg_swz(b)) * 16u;
+      dma16(rx, buf + (uint32_t)(kWoSegs + wave * (XR / 2) + 8 * j) * 128u,
+            b * (uint32_t)(a.x_sb * 2) + (uint32_t)(c * 256) + l * 128u + q16);
+    }
+  };
+  // Fragment of K-step st (0..7) of a chunk: row `row` at segment `seg`,
+  // 16-byte chunk 2 (st % 4) + hh of its line.
+  const uint32_t r32 = (uint32_t)(lane & 31);
+  auto frag = [&](const char LDS_AS* buf, uint32_t seg, uint32_t row, int st) __attribute__((always_inline)) {
+    const uint32_t c = (uint32_t)(2 * (st & 3) + hh);
+    return *(const bf16x8 LDS_AS*)(buf + seg * 128u + ((c ^ seg_swz(row)) * 16u));
+  };
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+  issue(0);
+  issue(1);
+  for (int it = 0; it < kNch; ++it) {
+    // This wave's loads of step it are in when at most step it + 1's are
+    // outstanding; after the barrier every wave's are, and every wave is done
+    // with buffer (it + 2) % 3, read in the previous step.
+    if (it + 1 < kNch) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDpc) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 2 < kNch) issue(it + 2);
+    const char LDS_AS* buf = (const char LDS_AS*)smem + (it % 3) * kBufSegs * 128;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const uint32_t l = (uint32_t)(st >> 2);
+      const bf16x8 af = frag(buf, (uint32_t)(wave * 64) + l * 32u + r32, r32, st);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const uint32_t b = (uint32_t)(32 * n) + r32;
+        acc[n] = mfma32(af, frag(buf, (uint32_t)kWoSegs + l * (uint32_t)XR + b, b, st), acc[n]);
+      }
+    }
+  }
+  // acc[n][v] of lane l: output o0 + 8 (v / 4) + 4 (l / 32) + v % 4, batch row
+  // 32 n + l % 32; four consecutive outputs per store.
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int b = 32 * n + (lane & 31);
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int m = 8 * g4 + 4 * hh;
+      if (m < kOpRows && b < a.B)
+        *reinterpret_cast<float4*>(a.part + ((int64_t)q * a.B + b) * kWoOut + o0 + m) =
+            float4{acc[n][4 * g4], acc[n][4 * g4 + 1], acc[n][4 * g4 + 2], acc[n][4 * g4 + 3]};
+    }
+  }
+}
+
+// The quarters' partial sums of 8 consecutive outputs per thread, added in
+// quarter order and rounded to bf16.
+__global__ __launch_bounds__(256) void output_proj_reduce_kernel(const OutProjArgs a) {
+  constexpr int kPer = kWoOut / 8;
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (i >= a.B * kPer) return;
+  const int b = i / kPer, o = (i % kPer) * 8;
+  float s[8];
+#pragma unroll
+  for (int qq = 0; qq < kOpSplit; ++qq) {
+    const float4* p = reinterpret_cast<const float4*>(a.part + ((int64_t)qq * a.B + b) * kWoOut + o);
+    const float4 v0 = p[0], v1 = p[1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = qq == 0 ? v[e] : s[e] + v[e];
+  }
+  uint16_t* dst = a.out + (int64_t)b * a.out_sb + o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = __builtin_bit_cast(uint16_t, (__bf16)s[e]);
+}
+
+// ---------------------------------------------------------------------------
 // Output-projection weight repack (one-time set-up): packed[g][c][r][k] =
 // wo[28 g + r][256 c + k] for the 256 workgroups g, 64 chunks c, 28 rows r
 // and 256 columns k, 16 bytes per thread.
@@ -1745,6 +1878,16 @@ int launch_output_proj(const OutProjArgs& a, void* stream) {
     if (a.B <= 32) hipLaunchKernelGGL((output_proj_kernel<1, false>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((output_proj_kernel<2, false>), grid, dim3(256), 0, st, a);
   }
+  return (int)hipGetLastError();
+}
+
+int launch_output_proj_split(const OutProjArgs& a, void* stream) {
+  static_assert(kWoOut == 64 * 4 * kOpRows, "64 groups of four output tiles");
+  const hipStream_t st = (hipStream_t)stream;
+  if (a.B <= 32) hipLaunchKernelGGL((output_proj_split_kernel<1>), dim3(256), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((output_proj_split_kernel<2>), dim3(256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(output_proj_reduce_kernel, dim3((unsigned)((a.B * (kWoOut / 8) + 255) / 256)), dim3(256), 0, st,
+                     a);
   return (int)hipGetLastError();
 }
 

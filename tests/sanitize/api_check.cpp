@@ -27,6 +27,7 @@ int launch_value_up(const ValueUpArgs& a, void*) { last_vu = a; ++n_launch; retu
 int launch_dequant(const DequantArgs&, void*) { ++n_launch; return 0; }
 int launch_output_proj(const OutProjArgs& a, void*) { last_oproj = a; ++n_launch; return 0; }
 int launch_output_proj_pack(const uint16_t*, uint16_t*, void*) { ++n_launch; return 0; }
+int launch_output_proj_split(const OutProjArgs& a, void*) { last_oproj = a; ++n_launch; return 0; }
 int device_cu_count(int* cus) { *cus = 256; return 0; }
 static char fake_scratch[256] __attribute__((aligned(256)));
 int scratch_buffer(void** ptr) { *ptr = fake_scratch; return 0; }
@@ -116,6 +117,23 @@ int main() {
         mla::last_oproj.B == 6);
   CHECK(mla_output_proj_pack(P(F), P(F + 16), nullptr) == MLA_OK);
   CHECK(mla_output_proj_pack(P(F), P(F + 2), nullptr) == MLA_ERR_ALIGNMENT);
+  // Split over the inputs: a workspace of 4 x min(B, 64) x 7168 floats, one launch per 64 rows.
+  CHECK(mla_output_proj_split_workspace_bytes(1) == 4u * 7168u * 4u);
+  CHECK(mla_output_proj_split_workspace_bytes(100) == 4u * 64u * 7168u * 4u);
+  CHECK(mla_output_proj_split_workspace_bytes(0) == 0 && mla_output_proj_split_workspace_bytes(65537) == 0);
+  {
+    const size_t need = mla_output_proj_split_workspace_bytes(100);
+    const int b1 = mla::n_launch;
+    CHECK(mla_output_proj_split(P(F), 16384, P(F), P(F), 7168, 100, P(F), need, nullptr) == MLA_OK &&
+          mla::n_launch == b1 + 2 && mla::last_oproj.B == 36 && mla::last_oproj.part == P(F) &&
+          !mla::last_oproj.packed);
+    CHECK(mla_output_proj_split(P(F), 16384, P(F), P(F), 7168, 100, P(F), need - 1, nullptr) ==
+          MLA_ERR_WORKSPACE_TOO_SMALL);
+    CHECK(mla_output_proj_split(P(F), 16384, P(F), P(F), 7168, 100, nullptr, need, nullptr) == MLA_ERR_NULL_POINTER);
+    CHECK(mla_output_proj_split(P(F), 16384, P(F), P(F), 7168, 100, P(F + 4), need, nullptr) == MLA_ERR_ALIGNMENT);
+    CHECK(mla_output_proj_split(P(F), 16384, P(F), P(F), 7168, 0, P(F), need, nullptr) == MLA_ERR_BAD_DIM);
+    CHECK(mla_output_proj(P(F), 16384, P(F), P(F), 7168, 3, nullptr) == MLA_OK && mla::last_oproj.part == nullptr);
+  }
   for (int code = 0; code <= 8; ++code) CHECK(mla_status_string(code) != nullptr);
   puts("api sanitizer check: ok");
   return 0;

@@ -5,7 +5,11 @@ one rounding to bf16), across one and two 32-row batch tiles, a batch split
 over two launches (64 + 36 rows), and strided input and output rows.  The
 repacked weight (mla_output_proj_pack) is checked element for element against
 its definition, and mla_output_proj_packed bit for bit against
-mla_output_proj on the unpacked weight."""
+mla_output_proj on the unpacked weight.  mla_output_proj_split (the inputs
+split in four, fp32 partial sums added by a second launch) is checked
+against the oracle on the same rows, and on every row against
+mla_output_proj within two bf16 steps of the largest output (the two sum in
+different orders)."""
 import numpy as np
 import pytest
 import torch
@@ -73,3 +77,33 @@ def test_output_proj_packed_bit_identical(mla, inputs, B):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     ref = oracle.output_proj(x[[0, B - 1]], wo)
     assert rel_err(f64(b)[[0, B - 1], 0], ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("B,rows", [(1, [0]), (32, [0, 31]), (37, [0, 31, 32, 36]), (64, [5, 63]),
+                                    (100, [0, 63, 64, 99])])
+def test_output_proj_split(mla, inputs, B, rows):
+    x, wo, xg, wog = inputs
+    ws = torch.full((mla.mla_output_proj_split_workspace_bytes(B),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = mla.mla_output_proj_split(xg[:B], wog, ws)
+    plain = mla.mla_output_proj(xg[:B], wog)
+    torch.cuda.synchronize()
+    ref = oracle.output_proj(x[rows], wo)
+    assert rel_err(f64(out)[rows, 0], ref) <= REL_TOL
+    assert rel_err(f64(out), f64(plain)) <= 2 * 2.0 ** -8
+
+
+def test_output_proj_split_strided_and_errors(mla, inputs):
+    x, wo, xg, wog = inputs
+    B = 40
+    xs = torch.zeros((B, 16384 + 64), dtype=torch.bfloat16, device="cuda")
+    xs[:, :16384] = xg[:B].reshape(B, -1)
+    big = torch.full((B, 7200), 7.0, dtype=torch.bfloat16, device="cuda")
+    mla.mla_output_proj_split(xs[:, :16384], wog, out=big[:, :7168])
+    torch.cuda.synchronize()
+    rows = [0, 39]
+    ref = oracle.output_proj(x[rows], wo)
+    assert rel_err(f64(big)[rows, :7168], ref) <= REL_TOL
+    assert torch.all(big[:, 7168:] == 7.0)
+    small = torch.empty(mla.mla_output_proj_split_workspace_bytes(B) - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mla.MLAError):
+        mla.mla_output_proj_split(xg[:B], wog, small)
