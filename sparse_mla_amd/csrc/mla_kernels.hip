@@ -1780,25 +1780,31 @@ __global__ __launch_bounds__(256, 1) void output_proj_split_kernel(const OutProj
   }
 }
 
-// The quarters' partial sums of 8 consecutive outputs per thread, added in
-// quarter order and rounded to bf16.
+// The quarters' partial sums of 4 consecutive outputs per thread (one
+// 16-byte load per quarter, all four in flight together), added in quarter
+// order and rounded to bf16.
 __global__ __launch_bounds__(256) void output_proj_reduce_kernel(const OutProjArgs a) {
-  constexpr int kPer = kWoOut / 8;
+  constexpr int kPer = kWoOut / 4;
   const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
   if (i >= a.B * kPer) return;
-  const int b = i / kPer, o = (i % kPer) * 8;
-  float s[8];
+  const int b = i / kPer, o = (i % kPer) * 4;
+  float4 v[kOpSplit];
 #pragma unroll
-  for (int qq = 0; qq < kOpSplit; ++qq) {
-    const float4* p = reinterpret_cast<const float4*>(a.part + ((int64_t)qq * a.B + b) * kWoOut + o);
-    const float4 v0 = p[0], v1 = p[1];
-    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  for (int qq = 0; qq < kOpSplit; ++qq)
+    v[qq] = *reinterpret_cast<const float4*>(a.part + ((int64_t)qq * a.B + b) * kWoOut + o);
+  float4 s = v[0];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = qq == 0 ? v[e] : s[e] + v[e];
+  for (int qq = 1; qq < kOpSplit; ++qq) {
+    s.x += v[qq].x;
+    s.y += v[qq].y;
+    s.z += v[qq].z;
+    s.w += v[qq].w;
   }
   uint16_t* dst = a.out + (int64_t)b * a.out_sb + o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = __builtin_bit_cast(uint16_t, (__bf16)s[e]);
+  dst[0] = __builtin_bit_cast(uint16_t, (__bf16)s.x);
+  dst[1] = __builtin_bit_cast(uint16_t, (__bf16)s.y);
+  dst[2] = __builtin_bit_cast(uint16_t, (__bf16)s.z);
+  dst[3] = __builtin_bit_cast(uint16_t, (__bf16)s.w);
 }
 
 // ---------------------------------------------------------------------------
@@ -1886,7 +1892,7 @@ int launch_output_proj_split(const OutProjArgs& a, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
   if (a.B <= 32) hipLaunchKernelGGL((output_proj_split_kernel<1>), dim3(256), dim3(256), 0, st, a);
   else hipLaunchKernelGGL((output_proj_split_kernel<2>), dim3(256), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(output_proj_reduce_kernel, dim3((unsigned)((a.B * (kWoOut / 8) + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(output_proj_reduce_kernel, dim3((unsigned)((a.B * (kWoOut / 4) + 255) / 256)), dim3(256), 0, st,
                      a);
   return (int)hipGetLastError();
 }
