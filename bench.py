@@ -398,11 +398,20 @@ def main():
         d1.record(stream)
         torch.cuda.synchronize()
         sp_ms = d0.elapsed_time(d1) / args.steps
-        oproj["split_inputs"] = {"us": sp_ms * 1e3, "achieved_GBps": op_bytes / (sp_ms * 1e-3) / 1e9,
-                                 "frac_hbm": op_bytes / (sp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                 "kernel": "mla_output_proj_split (4 input quarters, then their sum)"}
+        split = {"us": sp_ms * 1e3, "bytes_per_launch": op_bytes, "achieved_GBps": op_bytes / (sp_ms * 1e-3) / 1e9,
+                 "frac_hbm": op_bytes / (sp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "tflops": 2.0 * B * HEADS * 128 * mla.MODEL_DIM / (sp_ms * 1e-3) / 1e12,
+                 "kernel": "mla_output_proj_split (4 input quarters, then their sum)",
+                 "weights": "bf16 [7168, 16384], 3 rotated copies"}
         log(f"output projection: {op_ms * 1e3:.2f} us ({oproj['achieved_GBps']:.0f} GB/s); "
             f"packed weight {pk_ms * 1e3:.2f} us; inputs split in four {sp_ms * 1e3:.2f} us")
+        # The call the library recommends at this batch leads: the split from
+        # 32 rows on, the single pass below; the others follow.
+        if B >= 32:
+            packed = oproj.pop("packed_weights")
+            oproj = dict(split, single_pass=oproj, packed_weights=packed)
+        else:
+            oproj["split_inputs"] = split
         del ox, wos, wps, oout, ows
     # fp8 weights: the same rotated steps with absorb and value-up reading the
     # block-scaled fp8 weight directly (16.8 MB of codes per step instead of
