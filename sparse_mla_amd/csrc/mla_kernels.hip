@@ -1680,10 +1680,11 @@ __global__ __launch_bounds__(256, 1) void output_proj_kernel(const OutProjArgs a
 // tile's 32 weight rows (rows past 28 masked) and a quarter of the x lines by
 // whole-line LDS-DMA into one of three buffers, two chunks ahead; the x lines
 // are shared by the four waves, so each chunk ends with a barrier.  Units are
-// numbered XCD-major (the quarters of a group share an XCD's L2 for x), and
-// the workgroups of XCD x start their walk at chunk 4 x (wrapping round), so
-// that the eight XCDs read different columns of wo at any moment while the
-// workgroups of one XCD read x's lines together.  Line l of row r at
+// numbered XCD-major: an XCD runs eight groups' four quarters, so each x
+// quarter is read by eight of its workgroups through its L2; and the
+// workgroups of XCD x start their walk at chunk 4 x (wrapping round), so that
+// the eight XCDs read different columns of wo at any moment while the
+// workgroups of one XCD read the same x lines together.  Line l of row r at
 // segment l * R + r of its region (R = 32 rows per wo tile, 32 NT x rows),
 // 16-byte chunk c at position c ^ seg_swz(r).  M = o, N = b, K = i.
 // ---------------------------------------------------------------------------
