@@ -27,6 +27,11 @@ such (one input set every step), and the attainable peaks measured on the
 same GPU (sparse_mla_amd/peaks.py: streaming read, the decode's row gather on
 random rows, dense bf16 MFMA) with the decode's fraction of them and the side
 of both ridges its intensity falls on.
+Timed apart from the step and not part of `value`: the sparse prefill
+(MFMA-bound, against the bf16 peak), the output projection after the step
+(the call recommended at the batch first, the others beside it), the step
+for 64, 32 and 16 heads, and, on the fp8 workload, the step reading the fp8
+weight codes directly.
 The CPU baseline runs the fp64 oracle (oracle/, test infrastructure) on a
 bounded sample of the same workload.
 
