@@ -63,7 +63,7 @@ typedef enum {
   MLA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                     */
   MLA_ERR_BAD_DIM = 2,             /* B, k_max, max_len or splits invalid */
   MLA_ERR_ALIGNMENT = 3,           /* base not 16-byte aligned / stride not 8 elements */
-  MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < mla_workspace_bytes(B, num_splits)   */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes below what the call's *_workspace_bytes gives */
   MLA_ERR_UNSUPPORTED = 5,         /* a stride too small for the fixed row widths, or a head count other than 16/32/64/128 */
   MLA_ERR_HIP = 6,                 /* a HIP call failed: see mla_last_hip_error()     */
   MLA_ERR_RANGE = 7,               /* one sequence's cache or q_pe span exceeds 2 GiB */
